@@ -1,0 +1,163 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant is a copy of oracle.c with one plausible mistake (a dropped term,
+a wrong sign, index or operand); it is compiled on the CPU and run through a
+battery of pins that never consult the oracle itself (golden bank maps,
+brute-force attention on the logical K/V, a closed form, store_kv's rejection
+of duplicate slots). The real oracle must pass the battery; every mutant must
+fail it. Mutants are chosen so that they stay memory-safe.
+"""
+from __future__ import annotations
+
+import math
+import os
+import tempfile
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+from paged_kv_attention_kvcache_amd import synth
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "causal_off_by_one": ("attend_span(qv, Kc, Vc, 0, pos + 1, D",
+                          "attend_span(qv, Kc, Vc, 0, pos, D"),
+    "gqa_head_map": ("int32_t h = kvh * G + g;\n          size_t qo = ((size_t)row",
+                     "int32_t h = g * Hkv + kvh;\n          size_t qo = ((size_t)row"),
+    "gather_offset": ("    int32_t off = pos % p->page_size;\n    for",
+                      "    int32_t off = (pos + 1) % p->page_size;\n    for"),
+    "gather_kv_head": ("size_t i = pool_index(p, bank, page, kvh, off, d);",
+                       "size_t i = pool_index(p, bank, page, 0, off, d);"),
+    "gather_k_from_v": ("Kc[(size_t)pos * D + d] = load_elem(p->elem_bytes, p->k, i);",
+                        "Kc[(size_t)pos * D + d] = load_elem(p->elem_bytes, p->v, i);"),
+    "dropped_scale": ("w[k - lo] = scale * s;", "w[k - lo] = s;"),
+    "no_max_shift": ("w[k - lo] = exp(w[k - lo] - m);", "w[k - lo] = exp(w[k - lo]);"),
+    "unnormalised": ("o[d] = acc[d] / l;", "o[d] = acc[d];"),
+    "lse_sign": ("if (lse) *lse = m + log(l);", "if (lse) *lse = m - log(l);"),
+    "bf16_shift": ("[idx] << 16;", "[idx] << 15;"),
+    "write_head": ("size_t dst = pool_index(p, bank, page, h, off, 0) * eb;",
+                   "size_t dst = pool_index(p, bank, page, 0, off, 0) * eb;"),
+    "write_offset": ("int32_t page = s / p->page_size, off = s % p->page_size;",
+                     "int32_t page = s / p->page_size, off = p->page_size - 1 - s % p->page_size;"),
+    "bank_unpacked": ("bank_of[t * num_layers + l] = held ? next++ : -1;",
+                      "bank_of[t * num_layers + l] = held ? t * num_layers + l : -1;"),
+    "combine_no_rescale": ("L += l[j] * exp(m[j] - M);", "L += l[j];"),
+    "partition_bound": ("int32_t lo = j * partition;", "int32_t lo = j * partition + (j > 0);"),
+    "prefill_position": ("int32_t pos = n - qlen + j;", "int32_t pos = j;"),
+    "no_dup_check": ("if (sorted[i] == sorted[i - 1])", "if (0)"),
+}
+
+
+def _pool(lib, layout):
+    bank_of, nb = oracle.bank_map(layout.num_planes, layout.num_layers, layout.rec_first,
+                                  layout.rec_count, lib=lib)
+    return oracle.Pool(layout.dtype, layout.page_size, layout.num_pages, layout.num_kv_heads,
+                       layout.head_dim, bank_of, nb, fill=synth.poison_value(layout.dtype))
+
+
+def _close(a, b, tol=1e-12):
+    return np.all(np.abs(np.asarray(a) - np.asarray(b)) <= tol)
+
+
+def battery(lib) -> list[str]:
+    """Names of the pins that fail (empty = all pass)."""
+    failed = []
+
+    # golden bank maps (hand-derived from the pages; tests/golden/bank_maps.txt)
+    try:
+        bo, nb = oracle.bank_map(32, 8, 2, 4, lib=lib)
+        ok = nb == 132 and bo[1, 2] == 8 and bo[31, 5] == 131 and bo[5, 0] == -1
+        bo, nb = oracle.bank_map(4, 24, 0, 24, lib=lib)
+        ok = ok and nb == 96 and bo[3, 23] == 95 and bo[1, 0] == 24
+    except oracle.OracleError:
+        ok = False
+    if not ok:
+        failed.append("bank_map")
+
+    # decode vs brute force, fp32 GQA and bf16 on a packed multi-plane pool
+    for dtype, P, pl in (("f32", 4, (0, 0)), ("bf16", 16, (2, 1))):
+        try:
+            case = synth.make_decode_case(1, dtype, 3, (17, 50), 4, 2, 8, page_size=P,
+                                          num_planes=3, num_layers=3, rec_first=1,
+                                          planes_layers=[pl])
+            pool = _pool(lib, case.layout)
+            bd = case.banks[pl]
+            oracle.kv_write(pool, *pl, bd.fill_k, bd.fill_v, bd.fill_slots, lib=lib)
+            oracle.kv_write(pool, *pl, bd.new_k, bd.new_v, bd.new_slots, lib=lib)
+            o, l = oracle.decode(pool, *pl, bd.q, case.page_table, case.seq_lens, lib=lib)
+            ok = True
+            for r in range(case.batch):
+                n = int(case.seq_lens[r])
+                bo_, bl_ = brute.attention(bd.q[r:r + 1], bd.logical_k[r], bd.logical_v[r],
+                                           np.array([n - 1]), 1 / math.sqrt(8))
+                ok = ok and _close(o[r], bo_[0]) and _close(l[r], bl_[0])
+            # split-K partials + combine
+            pm, pl_, pa = oracle.decode_partials(pool, *pl, bd.q, case.page_table,
+                                                 case.seq_lens, 16, 4, lib=lib)
+            o2, l2 = oracle.combine(np.repeat(-(-case.seq_lens // 16), 4), pm, pl_, pa, lib=lib)
+            ok = ok and _close(o2.reshape(o.shape), o, 1e-12) and _close(l2.reshape(l.shape), l)
+        except oracle.OracleError:
+            ok = False
+        if not ok:
+            failed.append(f"decode_{dtype}")
+
+    # prefill in chunks of 5 (suffix rows over cached keys) vs brute force
+    try:
+        case = synth.make_prefill_case(2, "bf16", [23, 11], 2, 1, 8, page_size=4)
+        pool = _pool(lib, case.layout)
+        ok = True
+        for ch in synth.chunk_schedule(case, 5):
+            oracle.kv_write(pool, 0, 0, ch.k, ch.v, ch.slots, lib=lib)
+            o, l = oracle.prefill(pool, 0, 0, ch.q, ch.cu_q_lens, case.page_table,
+                                  ch.seq_lens, 0.5, lib=lib)
+            for i, (r, lo) in enumerate(ch.rows):
+                a, b = ch.cu_q_lens[i], ch.cu_q_lens[i + 1]
+                bo_, bl_ = brute.attention(case.q[r][lo:lo + b - a], case.k[r], case.v[r],
+                                           np.arange(lo, lo + b - a), 0.5)
+                ok = ok and _close(o[a:b], bo_) and _close(l[a:b], bl_)
+    except oracle.OracleError:
+        ok = False
+    if not ok:
+        failed.append("prefill")
+
+    # store_kv rejects a duplicate slot
+    layout = synth.Layout("f32", 4, 3, 1, 4)
+    pool = _pool(lib, layout)
+    k = np.zeros((2, 1, 4), np.float32)
+    try:
+        oracle.kv_write(pool, 0, 0, k, k, [3, 3], lib=lib)
+        failed.append("dup_slot")
+    except oracle.OracleError as e:
+        if e.code != oracle.ORC_EDUP:
+            failed.append("dup_slot")
+    return failed
+
+
+def _build_variant(tmp, name, mutation):
+    src = open(SRC).read()
+    if mutation is not None:
+        old, new = mutation
+        assert src.count(old) == 1, f"mutation {name}: pattern must occur once"
+        src = src.replace(old, new)
+    path = os.path.join(tmp, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src)
+    out = os.path.join(tmp, f"lib{name}.so")
+    oracle.build(src=path, out=out, extra=["-I", os.path.dirname(SRC)])
+    return oracle.load(out)
+
+
+def test_real_oracle_passes_battery():
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = _build_variant(tmp, "real", None)
+        assert battery(lib) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        lib = _build_variant(tmp, name, MUTANTS[name])
+        assert battery(lib), f"planted mistake {name} passed every pin"
