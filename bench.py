@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one decode step of a looped model through every (plane, layer) bank
+in model order: for each bank, store_kv writes each request's newest token
+(paged_kv_write), then decode attention reads the whole context through the
+page table (paged_decode_attn: split-K partial kernel + combine kernel).
+
+Default workload (Ouro-style fixed depth): 24 layers x 4 loop planes = 96
+banks, batch 64, seq_lens uniform in [512, 2048], page size 16, 16 query / 8
+KV heads, head_dim 128, bf16, pages randomly permuted. Other workloads:
+--workload huginn (132 packed banks, MHA 32 heads, 78% aliased prompt pages),
+--workload longctx (batch 256, 8k-32k context, GQA 8, one bank), --workload
+prefill (chunked prefill, 8 x 512-token prompts, 32 heads).
+
+Prints one JSON line. `value` is logical KV bytes read by decode attention
+per second over the whole step (write + attention for every bank), with all
+inputs resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "paged decode attention KV GB/s (% of HBM peak); prefill TFLOP/s (% MFMA)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_attention_kvcache_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, launches_per_unit: float = 1.0):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when it was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------- workloads
+
+class DecodeWorkload:
+    """A multi-plane pool and one decode step's inputs, all on the device."""
+
+    def __init__(self, name, batch, seq_range, hq, hkv, D, planes, layers, rec_first,
+                 rec_count, order, alias=0.0, partition=0, seed=0, snapshot_banks=0):
+        import torch
+
+        import paged_kv_attention_kvcache_amd as pkv
+        from paged_kv_attention_kvcache_amd import synth
+
+        self.name, self.hq, self.hkv, self.D = name, hq, hkv, D
+        self.partition = partition or pkv.DEFAULT_PARTITION
+        rng = np.random.default_rng(seed)
+        if alias > 0:
+            prompts = rng.integers(seq_range[0], seq_range[1] + 1, size=batch)
+            self.seq = (prompts + 1).astype(np.int32)
+            shared = synth.alias_pages(prompts, alias, 16)
+        else:
+            self.seq = rng.integers(seq_range[0], seq_range[1] + 1, size=batch).astype(np.int32)
+            shared = None
+        self.table, self.num_pages, _ = synth.allocate_pages(rng, self.seq, 16,
+                                                             shared_pages=shared)
+        self.shared = shared
+        self.bank_of, self.nb = pkv.bank_map(planes, layers, rec_first, rec_count)
+        self.order = order  # [(plane, layer)] in model order
+        shape = (self.nb, self.num_pages, hkv, 16, D)
+        gb = 2 * np.prod(shape) * 2 / 1e9
+        log(f"[{name}] pool: {self.nb} banks x {self.num_pages} pages = {gb:.1f} GB")
+        k = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        v = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        synth.device_normal_(k, seed + 1)
+        synth.device_normal_(v, seed + 2)
+        self.pool = pkv.Pool(torch.bfloat16, self.num_pages, hkv, D, self.bank_of, self.nb,
+                             k=k, v=v)
+        nbk = len(order)
+        self.q = synth.device_normal_(torch.empty((nbk, batch, hq, D), dtype=torch.bfloat16,
+                                                  device="cuda"), seed + 3)
+        self.nk = synth.device_normal_(torch.empty((nbk, batch, hkv, D), dtype=torch.bfloat16,
+                                                   device="cuda"), seed + 4)
+        self.nv = synth.device_normal_(torch.empty((nbk, batch, hkv, D), dtype=torch.bfloat16,
+                                                   device="cuda"), seed + 5)
+        self.slots = torch.from_numpy(synth.slots_of_last(self.table, self.seq, 16)).cuda()
+        self.table_d = torch.from_numpy(self.table).cuda()
+        self.seq_d = torch.from_numpy(self.seq).cuda()
+        self.max_seq = int(self.seq.max())
+        self.out = torch.empty((batch, hq, D), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((batch, hq), dtype=torch.float32, device="cuda")
+        wsb = pkv.workspace_bytes(batch, hq, D, self.max_seq, self.partition)
+        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        self.pkv = pkv
+        # algorithmic bytes: each request reads its whole context (K and V)
+        self.kv_bytes_per_call = int(self.seq.astype(np.int64).sum()) * 2 * hkv * D * 2
+        uniq_pages = len(np.unique(np.concatenate(
+            [self.table[r, :-(-int(n) // 16)] for r, n in enumerate(self.seq)])))
+        self.unique_bytes_per_call = uniq_pages * 2 * hkv * 16 * D * 2
+        self.batch = batch
+        torch.cuda.synchronize()
+        # Host copies for the CPU baseline, taken before any library kernel runs.
+        self.snap = []
+        for i in range(min(snapshot_banks, len(order))):
+            b = int(self.bank_of[order[i]])
+            hb = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            self.snap.append((hb(k[b])[None], hb(v[b])[None], hb(self.q[i])))
+
+    def call(self, i, timing=None):
+        plane, layer = self.order[i]
+        pkv = self.pkv
+        pkv.kv_write(self.pool, plane, layer, self.nk[i], self.nv[i], self.slots)
+        if timing is not None:
+            timing[0].record()
+        pkv.decode(self.pool, plane, layer, self.q[i], self.table_d, self.seq_d, self.max_seq,
+                   partition=self.partition, out=self.out, lse=self.lse, workspace=self.ws)
+        if timing is not None:
+            timing[1].record()
+
+    def step(self):
+        for i in range(len(self.order)):
+            self.call(i)
+
+
+def make_workload(name, partition, snapshot_banks=0):
+    kw = dict(partition=partition, snapshot_banks=snapshot_banks)
+    if name == "ouro":
+        order = [(t, l) for t in range(4) for l in range(24)]
+        return DecodeWorkload("ouro", 64, (512, 2048), 16, 8, 128, 4, 24, 0, 24, order, **kw)
+    if name == "huginn":
+        order = [(0, 0), (0, 1)] + [(t, l) for t in range(32) for l in range(2, 6)] + \
+                [(0, 6), (0, 7)]
+        return DecodeWorkload("huginn", 16, (200, 2000), 32, 32, 128, 32, 8, 2, 4, order,
+                              alias=0.78, **kw)
+    if name == "longctx":
+        return DecodeWorkload("longctx", 256, (8192, 32768), 64, 8, 128, 1, 1, 0, 1, [(0, 0)],
+                              **kw)
+    raise SystemExit(f"unknown workload {name}")
+
+
+CONFIG_TEXT = {
+    "ouro": dict(workload="ouro_fixed_depth_decode", batch=64, seq_lens="uniform[512,2048]",
+                 planes=4, layers=24, banks=96, q_heads=16, kv_heads=8, head_dim=128,
+                 page_size=16),
+    "huginn": dict(workload="huginn_recurrent_depth_decode", batch=16,
+                   prompts="uniform[200,2000]", planes=32, layers=8, banks=132, q_heads=32,
+                   kv_heads=32, head_dim=128, page_size=16, aliased_prompt_pages=0.78),
+    "longctx": dict(workload="long_context_decode", batch=256, seq_lens="uniform[8192,32768]",
+                    planes=1, layers=1, banks=1, q_heads=64, kv_heads=8, head_dim=128,
+                    page_size=16),
+}
+
+
+# --------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl: DecodeWorkload, budget_s: float = 15.0):
+    """The fp64 oracle, as it stands, on whole bank calls of the same step
+    (host copies taken before any library kernel ran) until about budget_s of
+    CPU time; scaled to KV GB/s like the GPU value."""
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    cores = int(os.environ["OMP_NUM_THREADS"])
+    done_bytes, spent, calls = 0, 0.0, 0
+    bank_of = np.zeros((1, 1), np.int32)
+    for k, v, q in wl.snap:
+        op = oracle.Pool("bf16", 16, wl.num_pages, wl.hkv, wl.D, bank_of, 1, k, v)
+        t0 = time.perf_counter()
+        oracle.decode(op, 0, 0, q, wl.table, wl.seq)
+        spent += time.perf_counter() - t0
+        done_bytes += wl.kv_bytes_per_call
+        calls += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{calls} of {len(wl.order)} bank decode calls of one {wl.name} step "
+                      f"({wl.batch} requests, all heads), fp64, {spent:.1f} s"}
+
+
+# --------------------------------------------------------------------------- main
+
+def run_decode(args):
+    import torch
+
+    wl = make_workload(args.workload, args.partition,
+                       0 if args.no_cpu_baseline else args.cpu_banks)
+    nb = len(wl.order)
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    # Timed region: K whole steps, events on the stream the library launches on.
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        wl.step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # Per-launch timing of the decode call (partial + combine kernels), again
+    # over K steps, bracketing every decode call with events on the same stream.
+    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in range(nb * args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for i in range(nb):
+            wl.call(i, evs[s * nb + i])
+    torch.cuda.synchronize()
+    per_call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    avg_call_s = float(per_call_ms.mean()) / 1e3
+
+    step_bytes = wl.kv_bytes_per_call * nb
+    value = step_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = wl.kv_bytes_per_call / avg_call_s / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q, random page permutation)",
+        "config": dict(CONFIG_TEXT[wl.name], partition=wl.partition),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "tokens_planes_per_s": round(wl.batch * nb / (ms_per_step / 1e3), 1),
+        "decode_call_us": {"mean": round(float(per_call_ms.mean()) * 1e3, 2),
+                           "p10": round(float(np.percentile(per_call_ms, 10)) * 1e3, 2),
+                           "p90": round(float(np.percentile(per_call_ms, 90)) * 1e3, 2)},
+        "kv_bytes_per_call": wl.kv_bytes_per_call,
+        "unique_kv_bytes_per_call": wl.unique_bytes_per_call,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profiles(wl.name),
+                     "kernel": "decode call: decode_partial_valu + decode_reduce"},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ouro", choices=["ouro", "huginn", "longctx"])
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-banks", type=int, default=4,
+                    help="bank calls snapshotted for the CPU baseline (upper bound)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path "
+              f"has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_attention_kvcache_amd as pkv
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    pkv.lib()
+    log(f"device: {torch.cuda.get_device_name(0)}; workload {args.workload}")
+    res = run_decode(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * pagedkv -- paged-KV attention over a multi-plane page pool, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations follow two pages:
+ *   [FFM]   "Faster fuzzy minds" (dibbla.space, fast_subconscious)
+ *           - section "When scheduler does the work": the KV cache is a flat
+ *             pool of fixed-size slots addressed through
+ *             page_table[request, position]; a sequence's KV need not be
+ *             contiguous and two sequences may point at the same slots;
+ *             requests sharing a prompt prefix inherit its KV;
+ *           - section "So why is this hard for latent / looped models?":
+ *             each decode step appends one slot per request and runs one
+ *             query per request;
+ *           - section "LOTUS -- the one place I opened the scheduler":
+ *             store_kv scatters each token's K/V to the slots it is handed
+ *             (out_loc), so handing the same slots again overwrites in
+ *             place; re-running a span is an extend-prefill;
+ *           - section "Recurrent depth -- a deep model in a trench coat":
+ *             loop iteration t of weight layer l writes its own KV bank
+ *             t*L + l; a token keeps one position across all its banks.
+ *   [PR152] vllm-rlt pull 152, "[Huginn] Opt-in prefix caching with
+ *           position-keyed noise", section "Summary": each plane (loop
+ *           depth) holds only the layers it runs -- all layers at depth 0,
+ *           the recurrent layers deeper -- and banks are allocated only for
+ *           held layers (section "Notes", item #147).
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every buffer. The library allocates no
+ *     device memory and keeps no state between calls except a thread-local
+ *     error string.
+ *   - Asynchrony: device work is enqueued on `stream` (a hipStream_t passed
+ *     as void*; NULL = the null stream) and the call returns without
+ *     synchronising. Buffers must stay valid until the stream reaches the
+ *     work.
+ *   - Errors: a negative return means nothing was enqueued (except
+ *     PKV_ELAUNCH, which reports a failed launch). pkv_last_error() then
+ *     describes it. Device-resident tables (page ids, slots, seq_lens,
+ *     cu_q_lens) are not read on the host; values outside their contract
+ *     give unspecified results, but kernels clamp every index so that no
+ *     access leaves the buffers described here.
+ *
+ * Pool layout (device memory, one array for K and one for V):
+ *   element (bank, page, kv_head, offset, dim) of K is at
+ *   k_base[(((bank * num_pages + page) * num_kv_heads + kv_head)
+ *           * page_size + offset) * head_dim + dim]
+ *   and likewise for V. Banks are plane-major (bank ids come from bank_of).
+ *   A (page, kv_head) tile is page_size x head_dim contiguous elements
+ *   (4 KiB for bf16 at head_dim 128 and page_size 16).
+ *   Position pos of request r lives at page page_table[r * stride + pos /
+ *   page_size], offset pos % page_size, in every bank: one page table and
+ *   one slot mapping serve all planes and layers.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* null pointer, bad size or shape            */
+  PKV_EUNSUPPORTED = -2,  /* dtype / head_dim / page_size / group size  */
+  PKV_ENOTHELD = -3,      /* (plane, layer) owns no bank                */
+  PKV_EWORKSPACE = -4,    /* workspace too small                        */
+  PKV_ELAUNCH = -5        /* a kernel launch failed                     */
+};
+
+/* The pool descriptor. dtype is shared by the pool, q, k/v inputs and out.
+ * Supported: page_size 16; head_dim 64 or 128; num_q_heads / num_kv_heads
+ * in {1, 2, 4, 8}. bank_of is a HOST array [num_planes * num_layers] whose
+ * entry is the bank of (plane, layer) or -1 if the plane does not hold the
+ * layer. k_base / v_base are DEVICE pointers to num_banks * num_pages *
+ * num_kv_heads * page_size * head_dim elements each, 16-byte aligned. */
+typedef struct {
+  int32_t dtype;          /* pkv_dtype */
+  int32_t page_size;
+  int32_t num_pages;      /* pages per bank; ids in [0, num_pages) */
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_planes;
+  int32_t num_layers;
+  int32_t num_banks;
+  const int32_t *bank_of; /* HOST */
+  void *k_base;           /* DEVICE */
+  void *v_base;           /* DEVICE */
+} pkv_pool;
+
+/* Per-plane layer map ([FFM] recurrent depth; [PR152] summary). Plane 0
+ * holds every layer; planes >= 1 hold layers [rec_first, rec_first +
+ * rec_count), packed in plane-major order. rec_first = 0 and rec_count =
+ * num_layers gives bank = plane * num_layers + layer. Host only: fills the
+ * caller's bank_of [num_planes * num_layers] and returns the bank count, or a
+ * negative code. */
+int pkv_bank_map(int32_t num_planes, int32_t num_layers, int32_t rec_first,
+                 int32_t rec_count, int32_t *bank_of);
+
+/* Bytes of one of the pool's two arrays (K or V) for this descriptor. Host only. */
+size_t pkv_pool_bytes(const pkv_pool *pool);
+
+/* store_kv ([FFM] LOTUS): for every token t with slot s = slot_mapping[t] >=
+ * 0, copy k[t][h][:] and v[t][h][:] for every kv head h to page s / page_size,
+ * offset s % page_size of bank bank_of[plane_id][layer_id]. A byte copy: k and
+ * v are DEVICE [num_tokens][num_kv_heads][head_dim] in the pool dtype. A
+ * negative slot is skipped (padding). Writing a slot again in a later call
+ * overwrites it; the same slot twice in one call is unspecified; slots at or
+ * past num_pages * page_size are skipped. num_tokens 0 enqueues nothing. */
+int paged_kv_write(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                   const void *k, const void *v, const int32_t *slot_mapping,
+                   int32_t num_tokens, void *stream);
+
+/* Workspace bytes paged_decode_attn needs for these sizes (0 = library
+ * default partition). Host only. Layout, with P = ceil(max_seq_len /
+ * partition) partitions per row and rows = batch * num_q_heads:
+ *   float part_m[rows][P]; float part_l[rows][P]; float part_acc[rows][P][head_dim]
+ * each array starting 256-byte aligned, in that order. */
+size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                    int32_t head_dim, int32_t max_seq_len,
+                                    int32_t partition);
+
+/* Decode attention through the page table ([FFM] scheduler and looped-model
+ * sections: one query per request, the KV read through page_table). For each
+ * request r with n = seq_lens[r] and each q head h: the query q[r][h][:] sits
+ * at position n - 1 and attends keys 0..n-1 of kv head h / (num_q_heads /
+ * num_kv_heads) in bank bank_of[plane_id][layer_id]:
+ *   out[r][h][:] = sum_k softmax_k(scale * q . K_k) V_k, lse[r][h] = ln sum_k exp(scale q.K_k).
+ * Split-K: the context is cut into partitions of `partition` tokens (0 =
+ * 512, a multiple of 16); each partition's partials go to the workspace and a
+ * second kernel combines them in partition order (deterministic; results are
+ * bitwise repeatable and independent of physical page placement). Rows with
+ * n <= partition are finished by the first kernel.
+ *   q:          DEVICE [batch][num_q_heads][head_dim], pool dtype
+ *   page_table: DEVICE int32 [batch][page_table_stride] page ids
+ *   seq_lens:   DEVICE int32 [batch], each in [0, max_seq_len]
+ *   max_seq_len: HOST bound, <= page_table_stride * page_size
+ *   out:        DEVICE [batch][num_q_heads][head_dim], pool dtype (RNE from fp32)
+ *   lse:        DEVICE fp32 [batch][num_q_heads] natural log, or NULL
+ *   workspace:  DEVICE, >= paged_decode_workspace_bytes(...) bytes
+ * seq_len 0 gives out 0 and lse -inf. */
+int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                      const void *q, int32_t num_q_heads,
+                      const int32_t *page_table, int32_t page_table_stride,
+                      const int32_t *seq_lens, int32_t batch,
+                      int32_t max_seq_len, float scale, int32_t partition,
+                      void *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* The split-K combine on its own (the second kernel of paged_decode_attn,
+ * usable on partials gathered from elsewhere). For each row i = r *
+ * num_q_heads + h with n = seq_lens[r], combines partials j = 0 ..
+ * ceil(n / partition) - 1 in order. Partials are in base-2 units: part_m =
+ * log2(e) * (max score of the partition), part_l = sum 2^(log2(e) s - part_m),
+ * part_acc = sum 2^(log2(e) s - part_m) V. Output:
+ *   M = max_j m_j, L = sum_j l_j 2^(m_j - M), out = sum_j acc_j 2^(m_j - M) / L,
+ *   lse = ln(2) (M + log2 L).
+ * The arrays are laid out as in the workspace (rows x max_parts [x head_dim]).
+ * A row with no partial gets out 0, lse -inf. */
+int paged_decode_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads,
+                        int32_t head_dim, const int32_t *seq_lens,
+                        int32_t partition, int32_t max_parts,
+                        const float *part_m, const float *part_l,
+                        const float *part_acc, void *out, float *lse,
+                        void *stream);
+
+/* Chunked causal prefill over paged context ([FFM] LOTUS: an extend-prefill;
+ * [FFM] scheduler: a cache hit prefills only the suffix). Write-then-attend:
+ * the chunk's own K/V must already be in the pool (paged_kv_write first).
+ * Request r owns packed query rows cu_q_lens[r] .. cu_q_lens[r+1]-1; with
+ * q_len = cu_q_lens[r+1] - cu_q_lens[r] and n = seq_lens[r] (context held
+ * after this chunk, so q_len <= n), row j sits at position n - q_len + j and
+ * attends keys 0..n - q_len + j (inclusive causal mask) of its kv head:
+ *   q:          DEVICE [total_q][num_q_heads][head_dim], pool dtype
+ *   cu_q_lens:  DEVICE int32 [batch + 1], cu_q_lens[0] = 0, cu_q_lens[batch] = total_q
+ *   page_table, seq_lens: as for decode
+ *   max_q_len, max_seq_len: HOST bounds on q_len and n
+ *   out:        DEVICE [total_q][num_q_heads][head_dim]; lse fp32 [total_q][num_q_heads] or NULL */
+int paged_prefill_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                       const void *q, int32_t num_q_heads,
+                       const int32_t *cu_q_lens, int32_t total_q,
+                       const int32_t *page_table, int32_t page_table_stride,
+                       const int32_t *seq_lens, int32_t batch,
+                       int32_t max_q_len, int32_t max_seq_len, float scale,
+                       void *out, float *lse, void *stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

@@ -1,0 +1,231 @@
+"""Paged-KV attention over a multi-plane page pool, for MI355X (gfx950).
+
+A thin ctypes binding over the C-ABI in include/pagedkv.h (libpagedkv.so,
+built in-tree by ``build.py``). Every step of the path runs in the library's
+HIP kernels; this module only marshals torch tensors (device memory) and the
+current HIP stream into the C calls, and allocates outputs and the split-K
+workspace through torch when the caller does not pass them.
+
+If the library is missing, importing the binding functions raises: there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpagedkv.so")
+
+PKV_F32, PKV_BF16 = 0, 1
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOTHELD, PKV_EWORKSPACE, PKV_ELAUNCH = 0, -1, -2, -3, -4, -5
+DEFAULT_PARTITION = 512
+
+_lib = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_planes", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("num_banks", ctypes.c_int32),
+        ("bank_of", ctypes.c_void_p),
+        ("k_base", ctypes.c_void_p),
+        ("v_base", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = ("pkv_bank_map", "pkv_pool_bytes", "paged_kv_write", "paged_decode_workspace_bytes",
+           "paged_decode_attn", "paged_decode_reduce", "paged_prefill_attn", "pkv_last_error")
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run paged_kv_attention_kvcache_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.pkv_bank_map.argtypes = [i32, i32, i32, i32, P]
+        L.pkv_bank_map.restype = ctypes.c_int
+        L.pkv_pool_bytes.argtypes = [P]
+        L.pkv_pool_bytes.restype = sz
+        L.paged_kv_write.argtypes = [P, i32, i32, P, P, P, i32, P]
+        L.paged_kv_write.restype = ctypes.c_int
+        L.paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.paged_decode_workspace_bytes.restype = sz
+        L.paged_decode_attn.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, i32, ctypes.c_float,
+                                        i32, P, P, P, sz, P]
+        L.paged_decode_attn.restype = ctypes.c_int
+        L.paged_decode_reduce.argtypes = [i32, i32, i32, i32, P, i32, i32, P, P, P, P, P, P]
+        L.paged_decode_reduce.restype = ctypes.c_int
+        L.paged_prefill_attn.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, P, i32, i32, i32,
+                                         ctypes.c_float, P, P, P]
+        L.paged_prefill_attn.restype = ctypes.c_int
+        L.pkv_last_error.argtypes = []
+        L.pkv_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().pkv_last_error().decode()
+
+
+def _check(rc: int):
+    if rc < 0:
+        raise PagedKVError(rc, last_error())
+    return rc
+
+
+def bank_map(num_planes: int, num_layers: int, rec_first: int = 0,
+             rec_count: int | None = None) -> tuple[np.ndarray, int]:
+    """Per-plane layer map -> (bank_of [planes, layers] int32, num_banks)."""
+    if rec_count is None:
+        rec_count = num_layers - rec_first
+    out = np.full((num_planes, num_layers), -7, np.int32)
+    n = _check(lib().pkv_bank_map(num_planes, num_layers, rec_first, rec_count,
+                                  out.ctypes.data))
+    return out, n
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class Pool:
+    """A multi-plane page pool in device memory.
+
+    k, v: torch tensors [num_banks, num_pages, num_kv_heads, 16, head_dim] of
+    dtype float32 or bfloat16 on the GPU (allocated here if not given).
+    bank_of: [num_planes, num_layers] int32 (from ``bank_map``).
+    """
+
+    def __init__(self, dtype, num_pages: int, num_kv_heads: int, head_dim: int,
+                 bank_of: np.ndarray, num_banks: int, page_size: int = 16,
+                 k=None, v=None, device="cuda"):
+        torch = _torch()
+        self.torch_dtype = dtype
+        self.dtype = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
+        self.page_size, self.num_pages = page_size, num_pages
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.bank_of = np.ascontiguousarray(bank_of, dtype=np.int32)
+        self.num_planes, self.num_layers = self.bank_of.shape
+        self.num_banks = num_banks
+        shape = (num_banks, num_pages, num_kv_heads, page_size, head_dim)
+        if k is None:
+            k = torch.empty(shape, dtype=dtype, device=device)
+            v = torch.empty(shape, dtype=dtype, device=device)
+        assert tuple(k.shape) == shape and tuple(v.shape) == shape
+        assert k.dtype == dtype and v.dtype == dtype and k.is_contiguous() and v.is_contiguous()
+        self.k, self.v = k, v
+        self._st = _Pool(self.dtype, page_size, num_pages, num_kv_heads, head_dim,
+                         self.num_planes, self.num_layers, num_banks,
+                         self.bank_of.ctypes.data, k.data_ptr(), v.data_ptr())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._st)
+
+
+def kv_write(pool: Pool, plane: int, layer: int, k, v, slot_mapping, stream=None) -> None:
+    """store_kv: k, v [T, Hkv, D] (pool dtype, device), slot_mapping [T] int32."""
+    T = int(slot_mapping.shape[0])
+    _check(lib().paged_kv_write(pool.ref, plane, layer, _dptr(k), _dptr(v),
+                                _dptr(slot_mapping), T, _stream(stream)))
+
+
+def workspace_bytes(batch: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+                    partition: int = 0) -> int:
+    return int(lib().paged_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len,
+                                                  partition))
+
+
+def decode(pool: Pool, plane: int, layer: int, q, page_table, seq_lens, max_seq_len: int,
+           scale: float | None = None, partition: int = 0, out=None, lse=None,
+           workspace=None, with_lse: bool = True, stream=None):
+    """Decode attention. q [B, Hq, D]; page_table [B, stride] int32; seq_lens [B] int32.
+
+    Returns (out [B, Hq, D], lse [B, Hq] fp32 or None)."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(B, Hq, D, max_seq_len, partition)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().paged_decode_attn(pool.ref, plane, layer, _dptr(q), Hq, _dptr(page_table),
+                                   int(page_table.shape[1]), _dptr(seq_lens), B, max_seq_len,
+                                   float(scale), partition, _dptr(out), _dptr(lse),
+                                   _dptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def decode_reduce(dtype, seq_lens, partition: int, part_m, part_l, part_acc, out=None,
+                  lse=None, stream=None):
+    """Split-K combine. part_m/part_l [B, Hq, max_parts] fp32 (base-2 units),
+    part_acc [B, Hq, max_parts, D]."""
+    torch = _torch()
+    B, Hq, max_parts = part_m.shape
+    D = part_acc.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=dtype, device=part_m.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=part_m.device)
+    code = PKV_BF16 if dtype == torch.bfloat16 else PKV_F32
+    _check(lib().paged_decode_reduce(code, B, Hq, D, _dptr(seq_lens), partition, max_parts,
+                                     _dptr(part_m), _dptr(part_l), _dptr(part_acc), _dptr(out),
+                                     _dptr(lse), _stream(stream)))
+    return out, lse
+
+
+def prefill(pool: Pool, plane: int, layer: int, q, cu_q_lens, page_table, seq_lens,
+            max_q_len: int, max_seq_len: int, scale: float | None = None, out=None, lse=None,
+            with_lse: bool = True, stream=None):
+    """Chunked causal prefill. q [total_q, Hq, D] packed; cu_q_lens [B+1] int32."""
+    torch = _torch()
+    total_q, Hq, D = q.shape
+    B = int(seq_lens.shape[0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    _check(lib().paged_prefill_attn(pool.ref, plane, layer, _dptr(q), Hq, _dptr(cu_q_lens),
+                                    total_q, _dptr(page_table), int(page_table.shape[1]),
+                                    _dptr(seq_lens), B, max_q_len, max_seq_len, float(scale),
+                                    _dptr(out), _dptr(lse), _stream(stream)))
+    return out, lse

@@ -1,0 +1,79 @@
+// Device helpers shared by the gfx950 kernels: storage types, bf16 <-> fp32,
+// 16-byte vector loads, and DPP row reductions for 64-wide wavefronts.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kPage = 16;              // tokens per page
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage tags: Elem<T>::kBytes, widening of 16 bytes into fp32 lanes.
+struct F32 {
+  using storage = float;
+  static constexpr int kBytes = 4;
+};
+struct BF16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// 16 bytes -> fp32 values (8 for bf16, 4 for fp32).
+template <typename E> struct Vec;
+template <> struct Vec<BF16> {
+  static constexpr int kN = 8;
+  __device__ __forceinline__ static void widen(const uint4 &x, float *f) {
+    f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x);
+    f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
+    f[4] = bf16_lo(x.z); f[5] = bf16_hi(x.z);
+    f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
+  }
+};
+template <> struct Vec<F32> {
+  static constexpr int kN = 4;
+  __device__ __forceinline__ static void widen(const uint4 &x, float *f) {
+    f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
+    f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
+  }
+};
+
+// Store n fp32 values as the storage type (n = 8 for bf16 -> 16 bytes).
+template <typename E> __device__ __forceinline__ void store_row(typename E::storage *dst, const float *v, int n);
+template <> __device__ __forceinline__ void store_row<F32>(float *dst, const float *v, int n) {
+  for (int i = 0; i < n; ++i) dst[i] = v[i];
+}
+template <> __device__ __forceinline__ void store_row<BF16>(uint16_t *dst, const float *v, int n) {
+  for (int i = 0; i < n; ++i) dst[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+}
+
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N lanes (N in {8, 16, 32}); every lane of the
+// group gets the total. Fixed butterfly order, so results are repeatable.
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp<0x141>(x);  // row_half_mirror: the other quad of each 8
+  if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror: other 8 of each 16
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

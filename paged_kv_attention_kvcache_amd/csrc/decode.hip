@@ -1,0 +1,147 @@
+// Split-K paged decode attention for gfx950: partial kernel + fixed-order
+// combine kernel.
+//
+// One query per request sits at position seq_len - 1 and reads the whole
+// context through the page table ("Faster fuzzy minds", sections "When
+// scheduler does the work" and "So why is this hard for latent / looped
+// models?"). The context is cut into partitions of `partition` tokens; one
+// workgroup handles one (partition, kv head, request) and all query heads of
+// that kv head's GQA group, so every K/V byte is read from HBM once per call.
+// Partials (m, l, acc) are fp32 in base-2 units; the combine kernel folds
+// them in partition order. Rows whose context fits one partition are
+// finished directly by the partial kernel.
+#include "launch.hpp"
+#include "valu_span.hpp"
+
+namespace pkv {
+
+template <typename E, int D, int G>
+__global__ __launch_bounds__(kBlock) void decode_partial_valu(
+    const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
+    const typename E::storage *__restrict__ q, int32_t hq,
+    const int32_t *__restrict__ page_table, int32_t pt_stride,
+    const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale, int32_t partition,
+    int32_t max_parts, typename E::storage *__restrict__ out, float *__restrict__ lse,
+    float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc) {
+  using TL = Tile<E, D>;
+  __shared__ float2 lds_ml[kWaves * G];
+  __shared__ float lds_acc[kWaves * G * D];
+
+  const int j = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
+  const int n = min(max(seq_lens[r], 0), max_seq_len);
+  const int lo = j * partition;
+  if (j > 0 && lo >= n) return;  // partition past the context (whole block exits)
+  const int hi = min(lo + partition, n);
+
+  float qv[G][TL::kVecN];
+  load_q<E, D, G>(q + ((size_t)r * hq + (size_t)kvh * G) * D, qscale, qv);
+  valu_span<E, D, G>(kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, lo, hi,
+                     qv, lds_ml, lds_acc);
+
+  const bool single = n <= partition;
+  for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+    const int g = idx / D, d = idx % D;
+    float M, L, A;
+    combine_waves<G, D>(lds_ml, lds_acc, g, d, M, L, A);
+    const size_t rowh = (size_t)r * hq + (size_t)kvh * G + g;
+    if (single) {
+      const float o = (L > 0.f) ? A / L : 0.f;
+      store_row<E>(out + rowh * D + d, &o, 1);
+      if (lse && d == 0) lse[rowh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const size_t pj = rowh * max_parts + j;
+      part_acc[pj * D + d] = A;
+      if (d == 0) {
+        part_m[pj] = M;
+        part_l[pj] = L;
+      }
+    }
+  }
+}
+
+// Combine partitions 0 .. ceil(n / partition) - 1 of one (request, head)
+// row, in order. One thread per output dim.
+template <typename E>
+__global__ __launch_bounds__(128) void decode_reduce(
+    int32_t hq, int32_t D, const int32_t *__restrict__ seq_lens, int32_t max_seq_len,
+    int32_t partition, int32_t max_parts, const float *__restrict__ part_m,
+    const float *__restrict__ part_l, const float *__restrict__ part_acc,
+    typename E::storage *__restrict__ out, float *__restrict__ lse, int skip_single) {
+  const int row = blockIdx.x, r = row / hq;
+  const int n = min(max(seq_lens[r], 0), max_seq_len);
+  const int np = min((n + partition - 1) / partition, max_parts);
+  if (skip_single && np <= 1) return;
+  const float *pm = part_m + (size_t)row * max_parts;
+  const float *pl = part_l + (size_t)row * max_parts;
+  float M = -INFINITY;
+  for (int j = 0; j < np; ++j) M = fmaxf(M, pm[j]);
+  const float ms = (M == -INFINITY) ? 0.f : M;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float L = 0.f, A = 0.f;
+    for (int j = 0; j < np; ++j) {
+      const float f = fast_exp2(pm[j] - ms);
+      L = fmaf(pl[j], f, L);
+      A = fmaf(part_acc[((size_t)row * max_parts + j) * D + d], f, A);
+    }
+    const float o = (L > 0.f) ? A / L : 0.f;
+    store_row<E>(out + (size_t)row * D + d, &o, 1);
+    if (lse && d == 0) lse[row] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename E, int D, int G>
+static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
+  const dim3 grid(a.max_parts, a.bank.num_kv_heads, a.batch);
+  hipLaunchKernelGGL((decode_partial_valu<E, D, G>), grid, dim3(kBlock), 0, stream,
+                     static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
+                     a.bank.num_pages, a.bank.num_kv_heads,
+                     static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
+                     a.pt_stride, a.seq_lens, a.max_seq_len, a.scale * kLog2e, a.partition,
+                     a.max_parts, static_cast<typename E::storage *>(a.out), a.lse, a.part_m,
+                     a.part_l, a.part_acc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.max_parts > 1)
+    return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, D, a.seq_lens, a.max_seq_len,
+                         a.partition, a.max_parts, a.part_m, a.part_l, a.part_acc, a.out,
+                         a.lse, true, stream);
+  return hipSuccess;
+}
+
+template <typename E, int D>
+static hipError_t decode_by_group(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.num_q_heads / a.bank.num_kv_heads) {
+    case 1: return decode_valu<E, D, 1>(a, stream);
+    case 2: return decode_valu<E, D, 2>(a, stream);
+    case 4: return decode_valu<E, D, 4>(a, stream);
+    case 8: return decode_valu<E, D, 8>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (a.bank.dtype == 1)
+    return a.bank.head_dim == 128 ? decode_by_group<BF16, 128>(a, stream)
+                                  : decode_by_group<BF16, 64>(a, stream);
+  return a.bank.head_dim == 128 ? decode_by_group<F32, 128>(a, stream)
+                                : decode_by_group<F32, 64>(a, stream);
+}
+
+hipError_t launch_reduce(int32_t dtype, int32_t batch, int32_t hq, int32_t D,
+                         const int32_t *seq_lens, int32_t max_seq_len, int32_t partition,
+                         int32_t max_parts, const float *part_m, const float *part_l,
+                         const float *part_acc, void *out, float *lse, bool skip_single,
+                         hipStream_t stream) {
+  const dim3 grid(batch * hq), block(D < 128 ? D : 128);
+  if (dtype == 1)
+    hipLaunchKernelGGL(decode_reduce<BF16>, grid, block, 0, stream, hq, D, seq_lens,
+                       max_seq_len, partition, max_parts, part_m, part_l, part_acc,
+                       static_cast<uint16_t *>(out), lse, skip_single ? 1 : 0);
+  else
+    hipLaunchKernelGGL(decode_reduce<F32>, grid, block, 0, stream, hq, D, seq_lens,
+                       max_seq_len, partition, max_parts, part_m, part_l, part_acc,
+                       static_cast<float *>(out), lse, skip_single ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

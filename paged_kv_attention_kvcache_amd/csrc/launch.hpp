@@ -1,0 +1,69 @@
+// Internal launchers (host side) for the gfx950 kernels. Arguments are
+// validated by the C-ABI layer before any of these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// One bank of the pool: K and V base pointers already offset to the bank.
+struct Bank {
+  void *k;
+  void *v;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;  // 0 = fp32, 1 = bf16
+};
+
+hipError_t launch_kv_write(const Bank &b, const void *k, const void *v,
+                           const int32_t *slots, int32_t num_tokens,
+                           hipStream_t stream);
+
+struct DecodeArgs {
+  Bank bank;
+  const void *q;
+  int32_t num_q_heads;
+  const int32_t *page_table;
+  int32_t pt_stride;
+  const int32_t *seq_lens;
+  int32_t batch;
+  int32_t max_seq_len;
+  float scale;
+  int32_t partition;  // tokens, multiple of 16
+  int32_t max_parts;
+  void *out;
+  float *lse;
+  float *part_m, *part_l, *part_acc;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+hipError_t launch_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads,
+                         int32_t head_dim, const int32_t *seq_lens,
+                         int32_t max_seq_len, int32_t partition,
+                         int32_t max_parts, const float *part_m,
+                         const float *part_l, const float *part_acc, void *out,
+                         float *lse, bool skip_single, hipStream_t stream);
+
+struct PrefillArgs {
+  Bank bank;
+  const void *q;
+  int32_t num_q_heads;
+  const int32_t *cu_q_lens;
+  int32_t total_q;
+  const int32_t *page_table;
+  int32_t pt_stride;
+  const int32_t *seq_lens;
+  int32_t batch;
+  int32_t max_q_len;
+  int32_t max_seq_len;
+  float scale;
+  void *out;
+  float *lse;
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,248 @@
+// C-ABI of the paged-KV attention library: host-side validation, bank
+// addressing and launch. See include/pagedkv.h for the contract of each
+// entry point.
+#include "pagedkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return PKV_OK;
+}
+
+constexpr int kDefaultPartition = 512;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+// Validates the pool descriptor and resolves (plane, layer) to a bank.
+int resolve_bank(const pkv_pool *p, int32_t plane, int32_t layer, pkv::Bank *bank) {
+  if (!p) return fail(PKV_EINVAL, "pool is NULL");
+  if (p->dtype != PKV_F32 && p->dtype != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, "dtype %d not supported (0 = fp32, 1 = bf16)", p->dtype);
+  if (p->page_size != 16) return fail(PKV_EUNSUPPORTED, "page_size %d not supported (16)", p->page_size);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "head_dim %d not supported (64, 128)", p->head_dim);
+  if (p->num_pages <= 0 || p->num_kv_heads <= 0 || p->num_planes <= 0 || p->num_layers <= 0 ||
+      p->num_banks <= 0)
+    return fail(PKV_EINVAL, "pool sizes must be positive");
+  if (!p->bank_of || !p->k_base || !p->v_base)
+    return fail(PKV_EINVAL, "pool bank_of / k_base / v_base is NULL");
+  if ((reinterpret_cast<uintptr_t>(p->k_base) | reinterpret_cast<uintptr_t>(p->v_base)) & 15)
+    return fail(PKV_EINVAL, "pool arrays must be 16-byte aligned");
+  if (plane < 0 || plane >= p->num_planes || layer < 0 || layer >= p->num_layers)
+    return fail(PKV_EINVAL, "(plane %d, layer %d) outside %d x %d", plane, layer, p->num_planes,
+                p->num_layers);
+  const int32_t b = p->bank_of[(size_t)plane * p->num_layers + layer];
+  if (b < 0) return fail(PKV_ENOTHELD, "plane %d does not hold layer %d", plane, layer);
+  if (b >= p->num_banks) return fail(PKV_EINVAL, "bank %d >= num_banks %d", b, p->num_banks);
+  const size_t bank_elems =
+      (size_t)p->num_pages * p->num_kv_heads * p->page_size * p->head_dim;
+  const size_t off = (size_t)b * bank_elems * elem_bytes(p->dtype);
+  bank->k = static_cast<char *>(p->k_base) + off;
+  bank->v = static_cast<char *>(p->v_base) + off;
+  bank->num_pages = p->num_pages;
+  bank->num_kv_heads = p->num_kv_heads;
+  bank->head_dim = p->head_dim;
+  bank->dtype = p->dtype;
+  return PKV_OK;
+}
+
+int check_heads(const pkv_pool *p, int32_t hq) {
+  if (hq <= 0 || hq % p->num_kv_heads != 0)
+    return fail(PKV_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", hq,
+                p->num_kv_heads);
+  const int g = hq / p->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PKV_EUNSUPPORTED, "GQA group %d not supported (1, 2, 4, 8)", g);
+  return PKV_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(PKV_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_bank_map(int32_t num_planes, int32_t num_layers, int32_t rec_first, int32_t rec_count,
+                 int32_t *bank_of) {
+  if (num_planes <= 0 || num_layers <= 0 || rec_first < 0 || rec_count < 0 ||
+      rec_first + rec_count > num_layers || !bank_of)
+    return fail(PKV_EINVAL, "bad bank map request");
+  int32_t next = 0;
+  for (int32_t plane = 0; plane < num_planes; ++plane)
+    for (int32_t layer = 0; layer < num_layers; ++layer) {
+      const bool held = plane == 0 || (layer >= rec_first && layer < rec_first + rec_count);
+      bank_of[plane * num_layers + layer] = held ? next++ : -1;
+    }
+  ok();
+  return next;
+}
+
+size_t pkv_pool_bytes(const pkv_pool *p) {
+  if (!p || p->num_banks <= 0 || p->num_pages <= 0) return 0;
+  return (size_t)p->num_banks * p->num_pages * p->num_kv_heads * p->page_size * p->head_dim *
+         elem_bytes(p->dtype);
+}
+
+int paged_kv_write(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *k,
+                   const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                   void *stream) {
+  pkv::Bank bank;
+  int rc = resolve_bank(pool, plane_id, layer_id, &bank);
+  if (rc) return rc;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!k || !v || !slot_mapping) return fail(PKV_EINVAL, "k / v / slot_mapping is NULL");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+    return fail(PKV_EINVAL, "k and v must be 16-byte aligned");
+  return launched(pkv::launch_kv_write(bank, k, v, slot_mapping, num_tokens,
+                                       static_cast<hipStream_t>(stream)),
+                  "paged_kv_write");
+}
+
+size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_seq_len, int32_t partition) {
+  if (partition == 0) partition = kDefaultPartition;
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition <= 0)
+    return 0;
+  const size_t parts = max_seq_len > 0 ? (size_t)(max_seq_len + partition - 1) / partition : 1;
+  const size_t rows = (size_t)batch * num_q_heads;
+  return 2 * align_up(rows * parts * sizeof(float)) +
+         align_up(rows * parts * head_dim * sizeof(float));
+}
+
+int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
+                      int32_t num_q_heads, const int32_t *page_table, int32_t page_table_stride,
+                      const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float scale,
+                      int32_t partition, void *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  pkv::Bank bank;
+  int rc = resolve_bank(pool, plane_id, layer_id, &bank);
+  if (rc) return rc;
+  if ((rc = check_heads(pool, num_q_heads))) return rc;
+  if (batch <= 0) return fail(PKV_EINVAL, "batch %d <= 0", batch);
+  if (!q || !page_table || !seq_lens || !out) return fail(PKV_EINVAL, "q / page_table / seq_lens / out is NULL");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
+  if (page_table_stride <= 0) return fail(PKV_EINVAL, "page_table_stride %d <= 0", page_table_stride);
+  if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)page_table_stride * pool->page_size)
+    return fail(PKV_EINVAL, "max_seq_len %d outside [0, stride * page_size = %lld]", max_seq_len,
+                (long long)page_table_stride * pool->page_size);
+  if (partition == 0) partition = kDefaultPartition;
+  if (partition < 0 || partition % 16 != 0)
+    return fail(PKV_EINVAL, "partition %d must be a positive multiple of 16", partition);
+  const size_t need = paged_decode_workspace_bytes(batch, num_q_heads, pool->head_dim,
+                                                   max_seq_len, partition);
+  const int32_t max_parts = max_seq_len > 0 ? (max_seq_len + partition - 1) / partition : 1;
+  if (max_parts > 1 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (max_parts > 65535) return fail(PKV_EINVAL, "too many partitions (%d)", max_parts);
+
+  pkv::DecodeArgs a{};
+  a.bank = bank;
+  a.q = q;
+  a.num_q_heads = num_q_heads;
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.max_seq_len = max_seq_len;
+  a.scale = scale;
+  a.partition = partition;
+  a.max_parts = max_parts;
+  a.out = out;
+  a.lse = lse;
+  if (workspace) {
+    const size_t rows = (size_t)batch * num_q_heads;
+    char *ws = static_cast<char *>(workspace);
+    a.part_m = reinterpret_cast<float *>(ws);
+    a.part_l = reinterpret_cast<float *>(ws + align_up(rows * max_parts * sizeof(float)));
+    a.part_acc = reinterpret_cast<float *>(ws + 2 * align_up(rows * max_parts * sizeof(float)));
+  }
+  return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), "paged_decode_attn");
+}
+
+int paged_decode_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                        const int32_t *seq_lens, int32_t partition, int32_t max_parts,
+                        const float *part_m, const float *part_l, const float *part_acc,
+                        void *out, float *lse, void *stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "dtype %d", dtype);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d", head_dim);
+  if (batch <= 0 || num_q_heads <= 0 || partition <= 0 || max_parts <= 0)
+    return fail(PKV_EINVAL, "sizes must be positive");
+  if (!seq_lens || !part_m || !part_l || !part_acc || !out)
+    return fail(PKV_EINVAL, "NULL pointer");
+  const int64_t max_seq = (int64_t)partition * max_parts;
+  return launched(pkv::launch_reduce(dtype, batch, num_q_heads, head_dim, seq_lens,
+                                     (int32_t)(max_seq > 0x7fffffff ? 0x7fffffff : max_seq),
+                                     partition, max_parts, part_m, part_l, part_acc, out, lse,
+                                     false, static_cast<hipStream_t>(stream)),
+                  "paged_decode_reduce");
+}
+
+int paged_prefill_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
+                       int32_t num_q_heads, const int32_t *cu_q_lens, int32_t total_q,
+                       const int32_t *page_table, int32_t page_table_stride,
+                       const int32_t *seq_lens, int32_t batch, int32_t max_q_len,
+                       int32_t max_seq_len, float scale, void *out, float *lse, void *stream) {
+  pkv::Bank bank;
+  int rc = resolve_bank(pool, plane_id, layer_id, &bank);
+  if (rc) return rc;
+  if ((rc = check_heads(pool, num_q_heads))) return rc;
+  if (batch <= 0) return fail(PKV_EINVAL, "batch %d <= 0", batch);
+  if (total_q < 0) return fail(PKV_EINVAL, "total_q %d < 0", total_q);
+  if (total_q == 0) return ok();
+  if (!q || !cu_q_lens || !page_table || !seq_lens || !out)
+    return fail(PKV_EINVAL, "q / cu_q_lens / page_table / seq_lens / out is NULL");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
+  if (page_table_stride <= 0) return fail(PKV_EINVAL, "page_table_stride %d <= 0", page_table_stride);
+  if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)page_table_stride * pool->page_size)
+    return fail(PKV_EINVAL, "max_seq_len %d outside [0, stride * page_size]", max_seq_len);
+  if (max_q_len < 0 || max_q_len > max_seq_len)
+    return fail(PKV_EINVAL, "max_q_len %d outside [0, max_seq_len]", max_q_len);
+  pkv::PrefillArgs a{};
+  a.bank = bank;
+  a.q = q;
+  a.num_q_heads = num_q_heads;
+  a.cu_q_lens = cu_q_lens;
+  a.total_q = total_q;
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.max_q_len = max_q_len;
+  a.max_seq_len = max_seq_len;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  return launched(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "paged_prefill_attn");
+}
+
+const char *pkv_last_error(void) { return g_err; }
+
+}  // extern "C"

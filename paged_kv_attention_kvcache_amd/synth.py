@@ -133,6 +133,15 @@ def slots_of(page_table: np.ndarray, r: int, positions: np.ndarray, page_size: i
             + positions % page_size).astype(np.int32)
 
 
+def slots_of_last(page_table: np.ndarray, seq_lens: Sequence[int], page_size: int) -> np.ndarray:
+    """Slot of each request's newest token (position n - 1); -1 for n = 0."""
+    out = np.full(len(seq_lens), -1, np.int32)
+    for r, n in enumerate(seq_lens):
+        if n > 0:
+            out[r] = slots_of(page_table, r, np.array([int(n) - 1]), page_size)[0]
+    return out
+
+
 def alias_pages(prompt_lens: Sequence[int], frac: float, page_size: int) -> np.ndarray:
     """Shared full pages per request for an aliased-prefix workload."""
     p = np.asarray(prompt_lens, np.int64)
@@ -363,3 +372,17 @@ def prefix_writes(case: PrefillCase, upto: Sequence[int]):
         vs.append(case.v[r][positions])
         ss.append(slots_of(case.page_table, r, positions, case.layout.page_size))
     return np.concatenate(ks), np.concatenate(vs), np.concatenate(ss).astype(np.int32)
+
+
+def device_normal_(t, seed: int, scale: float = 1.0):
+    """Fill a device tensor in place with N(0, scale^2) from a seeded torch
+    generator on its device (for pools too large to draw on the host)."""
+    import torch
+
+    g = torch.Generator(device=t.device)
+    g.manual_seed(seed)
+    flat = t.view(-1)
+    step = 1 << 28  # draw in slices to bound the temporary
+    for i in range(0, flat.numel(), step):
+        flat[i:i + step].normal_(0.0, scale, generator=g)
+    return t

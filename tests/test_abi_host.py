@@ -1,0 +1,155 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point the
+header declares, and its host logic (bank map, workspace size, argument
+validation) behaves as documented. No kernel is launched here: every call
+below fails validation before anything is enqueued."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_kvcache_amd as pkv
+from paged_kv_attention_kvcache_amd import build as pkv_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pkv.LIB_PATH):
+        pkv_build.build()
+    return pkv.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[a-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = header_functions()
+    assert set(declared) == set(pkv.EXPORTS), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_library_is_gfx950_only(L):
+    # The offload bundle entries of the library this repository built name
+    # their target; every one must be gfx950.
+    blob = open(pkv.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx\w+)", blob))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_bank_map_matches_golden(L):
+    from test_oracle_pins import read_golden
+
+    for name, g in read_golden().items():
+        p = g["params"]
+        bank_of, nb = pkv.bank_map(p["planes"], p["layers"], p["rec_first"], p["rec_count"])
+        assert nb == g["num_banks"], name
+        for (pl, la), b in g["entries"].items():
+            assert bank_of[pl, la] == b, (name, pl, la)
+
+
+def test_bank_map_rejects(L):
+    with pytest.raises(pkv.PagedKVError):
+        pkv.bank_map(2, 4, 3, 2)
+
+
+def test_workspace_bytes(L):
+    # rows * parts floats for m and l, rows * parts * D for acc, 256-aligned
+    rows, parts, D = 3 * 8, 4, 128
+    need = L.paged_decode_workspace_bytes(3, 8, D, 2048, 512)
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == 2 * al(rows * parts * 4) + al(rows * parts * D * 4)
+    assert L.paged_decode_workspace_bytes(3, 8, D, 2048, 0) == need  # default 512
+    assert L.paged_decode_workspace_bytes(0, 8, D, 2048, 512) == 0
+
+
+def _pool(dtype=1, page_size=16, head_dim=128, planes=2, layers=3, rec=(0, 3), kv=2,
+          pages=8, ptr=1 << 20):
+    bank_of, nb = pkv.bank_map(planes, layers, *rec)
+    st = pkv._Pool(dtype, page_size, pages, kv, head_dim, planes, layers, nb,
+                   bank_of.ctypes.data, ptr, ptr)
+    return st, bank_of
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), pkv.PKV_EUNSUPPORTED),
+    (dict(page_size=8), pkv.PKV_EUNSUPPORTED),
+    (dict(head_dim=96), pkv.PKV_EUNSUPPORTED),
+    (dict(ptr=0), pkv.PKV_EINVAL),
+    (dict(ptr=FAKE + 4), pkv.PKV_EINVAL),
+])
+def test_pool_validation(L, kw, code):
+    st, keep = _pool(**kw)
+    rc = L.paged_kv_write(ctypes.byref(st), 0, 0, FAKE, FAKE, FAKE, 4, None)
+    assert rc == code
+    assert pkv.last_error()
+
+
+def test_not_held(L):
+    st, keep = _pool(planes=3, layers=4, rec=(1, 2))
+    assert L.paged_kv_write(ctypes.byref(st), 2, 0, FAKE, FAKE, FAKE, 1, None) == pkv.PKV_ENOTHELD
+    assert L.paged_decode_attn(ctypes.byref(st), 1, 3, FAKE, 4, FAKE, 4, FAKE, 1, 64, 1.0, 0,
+                               FAKE, None, None, 0, None) == pkv.PKV_ENOTHELD
+    assert L.paged_prefill_attn(ctypes.byref(st), 2, 3, FAKE, 4, FAKE, 8, FAKE, 4, FAKE, 1, 8,
+                                64, 1.0, FAKE, None, None) == pkv.PKV_ENOTHELD
+    assert L.paged_kv_write(ctypes.byref(st), 3, 0, FAKE, FAKE, FAKE, 1, None) == pkv.PKV_EINVAL
+
+
+def test_decode_validation(L):
+    st, keep = _pool(kv=2)
+    call = lambda **o: L.paged_decode_attn(
+        ctypes.byref(st), 0, 0, FAKE, o.get("hq", 4), FAKE, o.get("stride", 4), FAKE,
+        o.get("batch", 2), o.get("max_seq", 64), 1.0, o.get("part", 0), FAKE, None,
+        o.get("ws", None), o.get("ws_bytes", 0), None)
+    assert call(hq=3) == pkv.PKV_EINVAL           # not a multiple of Hkv
+    assert call(hq=6) == pkv.PKV_EUNSUPPORTED     # group 3
+    assert call(batch=0) == pkv.PKV_EINVAL
+    assert call(max_seq=65) == pkv.PKV_EINVAL     # beyond stride * page_size
+    assert call(part=24) == pkv.PKV_EINVAL        # not a multiple of 16
+    assert call(max_seq=64, part=16) == pkv.PKV_EWORKSPACE
+    assert call(max_seq=64, part=16, ws=FAKE, ws_bytes=16) == pkv.PKV_EWORKSPACE
+    assert "workspace" in pkv.last_error()
+
+
+def test_prefill_validation(L):
+    st, keep = _pool(kv=2)
+    call = lambda **o: L.paged_prefill_attn(
+        ctypes.byref(st), 0, 0, FAKE, o.get("hq", 2), FAKE, o.get("total", 8), FAKE,
+        o.get("stride", 4), FAKE, o.get("batch", 1), o.get("max_q", 8), o.get("max_seq", 64),
+        1.0, FAKE, None, None)
+    assert call(hq=5) == pkv.PKV_EINVAL
+    assert call(batch=0) == pkv.PKV_EINVAL
+    assert call(total=-1) == pkv.PKV_EINVAL
+    assert call(max_seq=80) == pkv.PKV_EINVAL
+    assert call(max_q=70) == pkv.PKV_EINVAL
+    assert call(total=0) == pkv.PKV_OK            # nothing to do, nothing enqueued
+
+
+def test_reduce_validation(L):
+    assert L.paged_decode_reduce(3, 1, 1, 128, FAKE, 512, 1, FAKE, FAKE, FAKE, FAKE, None,
+                                 None) == pkv.PKV_EUNSUPPORTED
+    assert L.paged_decode_reduce(1, 1, 1, 128, FAKE, 0, 1, FAKE, FAKE, FAKE, FAKE, None,
+                                 None) == pkv.PKV_EINVAL
+
+
+def test_write_zero_tokens_is_noop(L):
+    st, keep = _pool()
+    assert L.paged_kv_write(ctypes.byref(st), 0, 0, None, None, None, 0, None) == pkv.PKV_OK
