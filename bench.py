@@ -4,7 +4,7 @@
 A step is one decode step of a looped model through every (plane, layer) bank
 in model order: for each bank, store_kv writes each request's newest token
 (paged_kv_write), then decode attention reads the whole context through the
-page table (paged_decode_attn: split-K partial kernel + combine kernel).
+page table (paged_decode_attn: split-K partials, combined by the last workgroup).
 
 Default workload (Ouro-style fixed depth): 24 layers x 4 loop planes = 96
 banks, batch 64, seq_lens uniform in [512, 2048], page size 16, 16 query / 8
@@ -76,7 +76,7 @@ class DecodeWorkload:
         from paged_kv_attention_kvcache_amd import synth
 
         self.name, self.hq, self.hkv, self.D = name, hq, hkv, D
-        self.partition = partition or pkv.DEFAULT_PARTITION
+        self.partition = partition  # 0: the library's balanced split
         rng = np.random.default_rng(seed)
         if alias > 0:
             prompts = rng.integers(seq_range[0], seq_range[1] + 1, size=batch)
@@ -112,8 +112,8 @@ class DecodeWorkload:
         self.max_seq = int(self.seq.max())
         self.out = torch.empty((batch, hq, D), dtype=torch.bfloat16, device="cuda")
         self.lse = torch.empty((batch, hq), dtype=torch.float32, device="cuda")
-        wsb = pkv.workspace_bytes(batch, hq, D, self.max_seq, self.partition)
-        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        wsb = pkv.workspace_bytes(self.pool, batch, hq, self.max_seq, self.partition)
+        self.ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
         self.pkv = pkv
         # algorithmic bytes: each request reads its whole context (K and V)
         self.kv_bytes_per_call = int(self.seq.astype(np.int64).sum()) * 2 * hkv * D * 2
@@ -267,13 +267,38 @@ def run_decode(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(wl.name),
-                     "kernel": "decode call: decode_partial_valu + decode_reduce"},
+                     "kernel": "decode_partial_valu (split-K + in-kernel combine)"},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     return res
+
+
+def run_probe(kind: str):
+    """Plain copy / read of a buffer of known size, to calibrate the HBM byte
+    counters (FETCH_SIZE, WRITE_SIZE) and to give the achievable bandwidth."""
+    import torch
+
+    nbytes = 1 << 30
+    x = torch.empty(nbytes // 8, dtype=torch.int64, device="cuda").random_()
+    y = torch.empty_like(x)
+    fn = (lambda: y.copy_(x)) if kind == "copy" else (lambda: x.max())
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    moved = (2 if kind == "copy" else 1) * nbytes
+    return {"probe": kind, "bytes_per_launch": nbytes, "read_bytes": nbytes,
+            "write_bytes": nbytes if kind == "copy" else 0, "ms": round(ms, 4),
+            "GBps": round(moved / ms / 1e6, 1)}
 
 
 def main():
@@ -285,6 +310,8 @@ def main():
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--probe", choices=["copy", "read"], default=None,
+                    help="time a plain copy/read of 1 GiB instead (counter calibration)")
     ap.add_argument("--cpu-banks", type=int, default=4,
                     help="bank calls snapshotted for the CPU baseline (upper bound)")
     args = ap.parse_args()
@@ -299,6 +326,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     pkv.lib()
+    if args.probe:
+        print(json.dumps(run_probe(args.probe)), flush=True)
+        return
     log(f"device: {torch.cuda.get_device_name(0)}; workload {args.workload}")
     res = run_decode(args)
     print(json.dumps(res), flush=True)

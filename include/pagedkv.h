@@ -115,13 +115,11 @@ int paged_kv_write(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                    const void *k, const void *v, const int32_t *slot_mapping,
                    int32_t num_tokens, void *stream);
 
-/* Workspace bytes paged_decode_attn needs for these sizes (0 = library
- * default partition). Host only. Layout, with P = ceil(max_seq_len /
- * partition) partitions per row and rows = batch * num_q_heads:
- *   float part_m[rows][P]; float part_l[rows][P]; float part_acc[rows][P][head_dim]
- * each array starting 256-byte aligned, in that order. */
-size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
-                                    int32_t head_dim, int32_t max_seq_len,
+/* Workspace bytes paged_decode_attn needs for these sizes on the current
+ * device. Host only (it may query the device's compute-unit count and the
+ * decode kernel's occupancy). 0 for invalid sizes. */
+size_t paged_decode_workspace_bytes(const pkv_pool *pool, int32_t batch,
+                                    int32_t num_q_heads, int32_t max_seq_len,
                                     int32_t partition);
 
 /* Decode attention through the page table ([FFM] scheduler and looped-model
@@ -130,18 +128,27 @@ size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
  * at position n - 1 and attends keys 0..n-1 of kv head h / (num_q_heads /
  * num_kv_heads) in bank bank_of[plane_id][layer_id]:
  *   out[r][h][:] = sum_k softmax_k(scale * q . K_k) V_k, lse[r][h] = ln sum_k exp(scale q.K_k).
- * Split-K: the context is cut into partitions of `partition` tokens (0 =
- * 512, a multiple of 16); each partition's partials go to the workspace and a
- * second kernel combines them in partition order (deterministic; results are
- * bitwise repeatable and independent of physical page placement). Rows with
- * n <= partition are finished by the first kernel.
+ * Work split (the fp32 partials (m, l, acc) of a split context are folded in
+ * position order by a combine kernel, so results are bitwise repeatable and
+ * independent of physical page placement):
+ *   partition > 0 (a multiple of 16): fixed partitions of that many tokens,
+ *     one workgroup per (partition, kv head, request).
+ *   partition 0 (library default), chosen per call:
+ *     - whole contexts, one workgroup per (request, kv head), when
+ *       batch * num_kv_heads >= 512 and max_seq_len <= 4096 (no partials,
+ *       no combine);
+ *     - otherwise a balanced split: the (request, kv head, page) sequence is
+ *       cut into one equal contiguous range per wave of the grid, so every
+ *       wave streams the same number of pages whatever the spread of
+ *       lengths (falls back to partition 512 when batch > 4096).
+ * Calls that share a workspace must not run concurrently.
  *   q:          DEVICE [batch][num_q_heads][head_dim], pool dtype
  *   page_table: DEVICE int32 [batch][page_table_stride] page ids
  *   seq_lens:   DEVICE int32 [batch], each in [0, max_seq_len]
  *   max_seq_len: HOST bound, <= page_table_stride * page_size
  *   out:        DEVICE [batch][num_q_heads][head_dim], pool dtype (RNE from fp32)
  *   lse:        DEVICE fp32 [batch][num_q_heads] natural log, or NULL
- *   workspace:  DEVICE, >= paged_decode_workspace_bytes(...) bytes
+ *   workspace:  DEVICE scratch, >= paged_decode_workspace_bytes(...) bytes
  * seq_len 0 gives out 0 and lse -inf. */
 int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                       const void *q, int32_t num_q_heads,
@@ -151,8 +158,9 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                       void *out, float *lse, void *workspace,
                       size_t workspace_bytes, void *stream);
 
-/* The split-K combine on its own (the second kernel of paged_decode_attn,
- * usable on partials gathered from elsewhere). For each row i = r *
+/* The split-K combine for fixed partitions on its own (the second kernel of
+ * paged_decode_attn with partition > 0, usable on partials gathered from
+ * elsewhere, e.g. other devices). For each row i = r *
  * num_q_heads + h with n = seq_lens[r], combines partials j = 0 ..
  * ceil(n / partition) - 1 in order. Partials are in base-2 units: part_m =
  * log2(e) * (max score of the partition), part_l = sum 2^(log2(e) s - part_m),

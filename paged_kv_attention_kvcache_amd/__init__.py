@@ -67,7 +67,7 @@ def lib():
         L.pkv_pool_bytes.restype = sz
         L.paged_kv_write.argtypes = [P, i32, i32, P, P, P, i32, P]
         L.paged_kv_write.restype = ctypes.c_int
-        L.paged_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.paged_decode_workspace_bytes.argtypes = [P, i32, i32, i32, i32]
         L.paged_decode_workspace_bytes.restype = sz
         L.paged_decode_attn.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, i32, ctypes.c_float,
                                         i32, P, P, P, sz, P]
@@ -162,9 +162,9 @@ def kv_write(pool: Pool, plane: int, layer: int, k, v, slot_mapping, stream=None
                                 _dptr(slot_mapping), T, _stream(stream)))
 
 
-def workspace_bytes(batch: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+def workspace_bytes(pool: "Pool", batch: int, num_q_heads: int, max_seq_len: int,
                     partition: int = 0) -> int:
-    return int(lib().paged_decode_workspace_bytes(batch, num_q_heads, head_dim, max_seq_len,
+    return int(lib().paged_decode_workspace_bytes(pool.ref, batch, num_q_heads, max_seq_len,
                                                   partition))
 
 
@@ -182,7 +182,7 @@ def decode(pool: Pool, plane: int, layer: int, q, page_table, seq_lens, max_seq_
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    need = workspace_bytes(B, Hq, D, max_seq_len, partition)
+    need = workspace_bytes(pool, B, Hq, max_seq_len, partition)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()

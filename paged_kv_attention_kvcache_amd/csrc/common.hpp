@@ -50,6 +50,38 @@ template <> struct Vec<F32> {
   }
 };
 
+// A lane's 16-byte chunk of a query row, kept in the form the q.k dot
+// product consumes: packed bf16 pairs (v_dot2_f32_bf16) or fp32.
+template <typename E> struct QChunk;
+template <> struct QChunk<BF16> {
+  uint32_t w[4];
+  __device__ __forceinline__ void set(const uint4 &x) { w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w; }
+  // sum over the chunk of q * k, fp32 accumulation
+  __device__ __forceinline__ float dot(const uint4 &k) const {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0]),
+                                              __builtin_bit_cast(bf16x2, k.x), 0.f, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[1]),
+                                        __builtin_bit_cast(bf16x2, k.y), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[2]),
+                                        __builtin_bit_cast(bf16x2, k.z), a, false);
+    a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[3]),
+                                        __builtin_bit_cast(bf16x2, k.w), a, false);
+    return a;
+  }
+};
+template <> struct QChunk<F32> {
+  float f[4];
+  __device__ __forceinline__ void set(const uint4 &x) { Vec<F32>::widen(x, f); }
+  __device__ __forceinline__ float dot(const uint4 &k) const {
+    float a = f[0] * __uint_as_float(k.x);
+    a = fmaf(f[1], __uint_as_float(k.y), a);
+    a = fmaf(f[2], __uint_as_float(k.z), a);
+    a = fmaf(f[3], __uint_as_float(k.w), a);
+    return a;
+  }
+};
+
 // Store n fp32 values as the storage type (n = 8 for bf16 -> 16 bytes).
 template <typename E> __device__ __forceinline__ void store_row(typename E::storage *dst, const float *v, int n);
 template <> __device__ __forceinline__ void store_row<F32>(float *dst, const float *v, int n) {
@@ -75,5 +107,14 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte load marked non-temporal (global_load_dwordx4 ... nt): the data is
+// streamed once, and on gfx950 such loads sustain a markedly higher HBM
+// read rate than ordinary cached loads.
+__device__ __forceinline__ uint4 load_stream(const void *p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 }  // namespace pkv

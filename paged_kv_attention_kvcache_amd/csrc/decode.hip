@@ -8,12 +8,42 @@
 // workgroup handles one (partition, kv head, request) and all query heads of
 // that kv head's GQA group, so every K/V byte is read from HBM once per call.
 // Partials (m, l, acc) are fp32 in base-2 units; the combine kernel folds
-// them in partition order. Rows whose context fits one partition are
-// finished directly by the partial kernel.
+// them in partition order (deterministic). Rows whose context fits one
+// partition are finished directly by the partial kernel, and the combine
+// kernel is launched only when some row can span several partitions.
 #include "launch.hpp"
 #include "valu_span.hpp"
 
 namespace pkv {
+
+// Combines partitions 0 .. np-1 of row `rowh` (in order) for output dim d.
+__device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
+                                            const float *__restrict__ part_l,
+                                            const float *__restrict__ part_acc, size_t rowh,
+                                            int max_parts, int np, int D, int d, float &M,
+                                            float &L, float &A) {
+  const float *pm = part_m + rowh * max_parts;
+  const float *pl = part_l + rowh * max_parts;
+  M = -INFINITY;
+  for (int j = 0; j < np; ++j) M = fmaxf(M, pm[j]);
+  const float ms = (M == -INFINITY) ? 0.f : M;
+  L = 0.f;
+  A = 0.f;
+  for (int j = 0; j < np; ++j) {
+    const float f = fast_exp2(pm[j] - ms);
+    L = fmaf(pl[j], f, L);
+    A = fmaf(part_acc[(rowh * max_parts + j) * D + d], f, A);
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ void finish(typename E::storage *__restrict__ out,
+                                       float *__restrict__ lse, size_t rowh, int D, int d,
+                                       float M, float L, float A) {
+  const float o = (L > 0.f) ? A / L : 0.f;
+  store_row<E>(out + rowh * D + d, &o, 1);
+  if (lse && d == 0) lse[rowh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
 
 template <typename E, int D, int G>
 __global__ __launch_bounds__(kBlock) void decode_partial_valu(
@@ -29,32 +59,35 @@ __global__ __launch_bounds__(kBlock) void decode_partial_valu(
 
   const int j = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
   const int n = min(max(seq_lens[r], 0), max_seq_len);
+  const int np = min((n + partition - 1) / partition, max_parts);
   const int lo = j * partition;
-  if (j > 0 && lo >= n) return;  // partition past the context (whole block exits)
+  if (j > 0 && j >= np) return;  // partition past the context (whole block exits)
   const int hi = min(lo + partition, n);
 
-  float qv[G][TL::kVecN];
-  load_q<E, D, G>(q + ((size_t)r * hq + (size_t)kvh * G) * D, qscale, qv);
+  QChunk<E> qv[G];
+  load_q<E, D, G>(q + ((size_t)r * hq + (size_t)kvh * G) * D, qv);
   valu_span<E, D, G>(kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, lo, hi,
-                     qv, lds_ml, lds_acc);
+                     qv, qscale, lds_ml, lds_acc);
 
-  const bool single = n <= partition;
+  const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
+  if (np <= 1) {  // the whole context in one partition: finish here
+    for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+      const int g = idx / D, d = idx % D;
+      float M, L, A;
+      combine_waves<G, D>(lds_ml, lds_acc, g, d, M, L, A);
+      finish<E>(out, lse, row0 + g, D, d, M, L, A);
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
     const int g = idx / D, d = idx % D;
     float M, L, A;
     combine_waves<G, D>(lds_ml, lds_acc, g, d, M, L, A);
-    const size_t rowh = (size_t)r * hq + (size_t)kvh * G + g;
-    if (single) {
-      const float o = (L > 0.f) ? A / L : 0.f;
-      store_row<E>(out + rowh * D + d, &o, 1);
-      if (lse && d == 0) lse[rowh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
-    } else {
-      const size_t pj = rowh * max_parts + j;
-      part_acc[pj * D + d] = A;
-      if (d == 0) {
-        part_m[pj] = M;
-        part_l[pj] = L;
-      }
+    const size_t pj = (row0 + g) * max_parts + j;
+    part_acc[pj * D + d] = A;
+    if (d == 0) {
+      part_m[pj] = M;
+      part_l[pj] = L;
     }
   }
 }
@@ -70,22 +103,11 @@ __global__ __launch_bounds__(128) void decode_reduce(
   const int row = blockIdx.x, r = row / hq;
   const int n = min(max(seq_lens[r], 0), max_seq_len);
   const int np = min((n + partition - 1) / partition, max_parts);
-  if (skip_single && np <= 1) return;
-  const float *pm = part_m + (size_t)row * max_parts;
-  const float *pl = part_l + (size_t)row * max_parts;
-  float M = -INFINITY;
-  for (int j = 0; j < np; ++j) M = fmaxf(M, pm[j]);
-  const float ms = (M == -INFINITY) ? 0.f : M;
+  if (skip_single && np <= 1) return;  // finished by the partial kernel
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float L = 0.f, A = 0.f;
-    for (int j = 0; j < np; ++j) {
-      const float f = fast_exp2(pm[j] - ms);
-      L = fmaf(pl[j], f, L);
-      A = fmaf(part_acc[((size_t)row * max_parts + j) * D + d], f, A);
-    }
-    const float o = (L > 0.f) ? A / L : 0.f;
-    store_row<E>(out + (size_t)row * D + d, &o, 1);
-    if (lse && d == 0) lse[row] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+    float M, L, A;
+    combine_row(part_m, part_l, part_acc, row, max_parts, np, D, d, M, L, A);
+    finish<E>(out, lse, row, D, d, M, L, A);
   }
 }
 
@@ -100,12 +122,10 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
                      a.max_parts, static_cast<typename E::storage *>(a.out), a.lse, a.part_m,
                      a.part_l, a.part_acc);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.max_parts > 1)
-    return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, D, a.seq_lens, a.max_seq_len,
-                         a.partition, a.max_parts, a.part_m, a.part_l, a.part_acc, a.out,
-                         a.lse, true, stream);
-  return hipSuccess;
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, D, a.seq_lens, a.max_seq_len,
+                       a.partition, a.max_parts, a.part_m, a.part_l, a.part_acc, a.out, a.lse,
+                       true, stream);
 }
 
 template <typename E, int D>

@@ -1,0 +1,329 @@
+// Balanced split-K ("stream-K") paged decode attention for gfx950.
+//
+// The work of one decode call is the sequence of (request, kv head, page)
+// triples in request-major order; unit u = (request r, kv head h) owns
+// pages(r) = ceil(seq_len / 16) consecutive entries. Every wave of the grid
+// takes one contiguous, equal-sized range of that sequence, so all waves
+// stream the same number of pages (+-1) and stay busy until the end, whatever
+// the spread of sequence lengths. A wave folds the pages of a unit in order;
+// a unit that lies wholly inside one wave's range is finished by that wave,
+// otherwise each wave writes its segment as fp32 partials (at most two per
+// wave: the unit its range starts in, slot 0, and the unit it ends in, slot
+// 1) and the combine kernel folds a unit's segments in wave order, which is
+// position order. The split depends only on the sequence lengths and the
+// grid size, so results are bitwise repeatable and independent of where the
+// pages live.
+#include "launch.hpp"
+#include "valu_span.hpp"
+
+namespace pkv {
+
+__device__ __forceinline__ int pages_of(const int32_t *seq_lens, int r, int max_seq_len) {
+  const int n = min(max(seq_lens[r], 0), max_seq_len);
+  return (n + kPage - 1) / kPage;
+}
+
+// First entry of the range of wave w, for `total` entries over `nw` waves.
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t nw) {
+  return w * total / nw;
+}
+
+// Block-wide exclusive prefix over rows of hkv * pages(r): cum[r] for r <= B
+// (cum[B] = total), in LDS. Every thread of the block must call it.
+__device__ void row_prefix(const int32_t *__restrict__ seq_lens, int batch, int max_seq_len,
+                           int hkv, int *cum) {
+  __shared__ int wave_tot[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (batch + kBlock - 1) / kBlock;
+  const int r0 = tid * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i)
+    if (r0 + i < batch) sum += hkv * pages_of(seq_lens, r0 + i, max_seq_len);
+  int x = sum;  // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[w] = x;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += wave_tot[i];
+  int run = before + x - sum;  // exclusive prefix of this thread's first row
+  for (int i = 0; i < per; ++i) {
+    const int r = r0 + i;
+    if (r < batch) {
+      cum[r] = run;
+      run += hkv * pages_of(seq_lens, r, max_seq_len);
+    }
+  }
+  if (tid == kBlock - 1) cum[batch] = run;
+  __syncthreads();
+}
+
+// Partial slot (wave, slot) of head g: (m, l) and acc[D].
+__device__ __forceinline__ size_t part_index(int64_t wave, int slot, int G, int g) {
+  return ((size_t)wave * 2 + slot) * G + g;
+}
+
+template <typename E, int D, int G>
+__global__ __launch_bounds__(kBlock) void decode_stream_valu(
+    const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
+    const typename E::storage *__restrict__ q, int32_t hq,
+    const int32_t *__restrict__ page_table, int32_t pt_stride,
+    const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
+    typename E::storage *__restrict__ out, float *__restrict__ lse,
+    float2 *__restrict__ part_ml, float *__restrict__ part_acc) {
+  using TL = Tile<E, D>;
+  constexpr int N = TL::kVecN, LPT = TL::kLPT;
+  extern __shared__ int cum[];  // [batch + 1]
+  row_prefix(seq_lens, batch, max_seq_len, hkv, cum);
+
+  const int lane = threadIdx.x & 63;
+  const int row = lane / LPT, c = lane % LPT;
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t total = cum[batch];
+  int64_t s = range_start(gw, total, nw);
+  const int64_t e = range_start(gw + 1, total, nw);
+  if (s >= e) return;
+
+  // Unit holding entry s: the first r with cum[r + 1] > s.
+  int lo_r = 0, hi_r = batch - 1;
+  while (lo_r < hi_r) {
+    const int mid = (lo_r + hi_r) >> 1;
+    if (cum[mid + 1] > s) hi_r = mid; else lo_r = mid + 1;
+  }
+  int r = lo_r;
+  int pr = (cum[r + 1] - cum[r]) / hkv;
+  int kvh = (int)((s - cum[r]) / pr);
+  int p = (int)((s - cum[r]) % pr);
+  int slot = 0;
+  while (s < e) {
+    const int len = (int)min((int64_t)(pr - p), e - s);
+    const int n = min(max(seq_lens[r], 0), max_seq_len);
+    QChunk<E> qv[G];
+    load_q<E, D, G>(q + ((size_t)r * hq + (size_t)kvh * G) * D, qv);
+    SpanState<E, D, G> st;
+    reset(st);
+    wave_span<E, D, G>(st, kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, p,
+                       len, 1, 0, n, qv, qscale);
+    merge_rows(st);
+    if (row == 0) {
+      const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
+      if (p == 0 && len == pr) {  // the whole unit: finish here
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float inv = st.l[g] > 0.f ? 1.f / st.l[g] : 0.f;
+          float o[N];
+#pragma unroll
+          for (int e2 = 0; e2 < N; ++e2) o[e2] = st.acc[g][e2] * inv;
+          store_row<E>(out + (row0 + g) * D + c * N, o, N);
+          if (lse && c == 0)
+            lse[row0 + g] = st.l[g] > 0.f ? (st.m[g] + log2f(st.l[g])) * kLn2 : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const size_t pi = part_index(gw, slot, G, g);
+#pragma unroll
+          for (int e2 = 0; e2 < N; ++e2) part_acc[pi * D + c * N + e2] = st.acc[g][e2];
+          if (c == 0) part_ml[pi] = make_float2(st.m[g], st.l[g]);
+        }
+      }
+    }
+    s += len;
+    slot = 1;
+    p += len;
+    if (p == pr) {
+      p = 0;
+      if (++kvh == hkv) {
+        kvh = 0;
+        do { ++r; } while (r < batch && cum[r + 1] == cum[r]);
+        if (r < batch) pr = (cum[r + 1] - cum[r]) / hkv;
+      }
+    }
+  }
+}
+
+// Finishes the units the stream kernel split across waves, and the units of
+// empty requests (out 0, lse -inf). One block per unit; segments are folded
+// in wave order. The (m, l) of up to kSegChunk segments at a time are staged
+// in LDS, so each thread's acc loads are independent of one another.
+constexpr int kSegChunk = 64;
+
+template <typename E, int G>
+__global__ __launch_bounds__(kBlock) void decode_stream_combine(
+    int32_t hkv, int32_t D, const int32_t *__restrict__ seq_lens, int32_t batch,
+    int32_t max_seq_len, int64_t nw, const float2 *__restrict__ part_ml,
+    const float *__restrict__ part_acc, typename E::storage *__restrict__ out,
+    float *__restrict__ lse) {
+  __shared__ int sums[2][kBlock];
+  __shared__ int seg_part[kSegChunk];  // part_index(wave, slot, G, 0) / G
+  __shared__ float2 seg_ml[kSegChunk][G];
+  const int u = blockIdx.x, r = u / hkv, kvh = u % hkv, tid = threadIdx.x;
+  int before = 0, all = 0;
+  for (int i = tid; i < batch; i += kBlock) {
+    const int v = hkv * pages_of(seq_lens, i, max_seq_len);
+    all += v;
+    if (i < r) before += v;
+  }
+  sums[0][tid] = before;
+  sums[1][tid] = all;
+  __syncthreads();
+  for (int off = kBlock / 2; off > 0; off >>= 1) {
+    if (tid < off) {
+      sums[0][tid] += sums[0][tid + off];
+      sums[1][tid] += sums[1][tid + off];
+    }
+    __syncthreads();
+  }
+  const int64_t total = sums[1][0];
+  const int pr = pages_of(seq_lens, r, max_seq_len);
+  const int64_t a = (int64_t)sums[0][0] + (int64_t)kvh * pr, b = a + pr;
+  const size_t row0 = (size_t)r * hkv * G + (size_t)kvh * G;
+  if (pr == 0) {
+    for (int idx = tid; idx < G * D; idx += kBlock) {
+      const float z = 0.f;
+      store_row<E>(out + (row0 + idx / D) * D + idx % D, &z, 1);
+      if (lse && idx % D == 0) lse[row0 + idx / D] = -INFINITY;
+    }
+    return;
+  }
+  // Wave holding entry t: the last w with range_start(w) <= t.
+  const int64_t w0 = ((a + 1) * nw - 1) / total, w1 = (b * nw - 1) / total;
+  if (w0 == w1) return;  // finished by the stream kernel
+
+  // Per-(g, d) running fold; chunks of segments are staged in LDS.
+  const int per_thread = (G * D + kBlock - 1) / kBlock;  // <= 4 (G * D <= 1024)
+  float M[4], L[4], A[4];
+  for (int i = 0; i < 4; ++i) { M[i] = -INFINITY; L[i] = 0.f; A[i] = 0.f; }
+  // range_start(w) = w*q + floor(w*rm / nw), stepped without divisions.
+  const int64_t qt = total / nw, rm = total % nw;
+  int64_t w = w0, start = range_start(w0, total, nw), frac = (w0 * rm) % nw;
+  while (w <= w1) {
+    // Collect up to kSegChunk non-empty waves (thread 0), in order.
+    __shared__ int nseg;
+    __shared__ int64_t next_w, next_start, next_frac;
+    if (tid == 0) {
+      int k = 0;
+      while (w <= w1 && k < kSegChunk) {
+        int64_t f2 = frac + rm, st2 = start + qt;
+        if (f2 >= nw) { f2 -= nw; st2 += 1; }
+        if (st2 > start) {  // non-empty range
+          const int slot = start >= a ? 0 : 1;
+          seg_part[k++] = (int)(w * 2 + slot);
+        }
+        ++w; start = st2; frac = f2;
+      }
+      nseg = k; next_w = w; next_start = start; next_frac = frac;
+    }
+    __syncthreads();
+    for (int i = tid; i < nseg * G; i += kBlock)
+      seg_ml[i / G][i % G] = part_ml[(size_t)seg_part[i / G] * G + i % G];
+    __syncthreads();
+    for (int i = 0; i < per_thread; ++i) {
+      const int idx = tid + i * kBlock;
+      if (idx >= G * D) break;
+      const int g = idx / D, d = idx % D;
+      float m = M[i];
+      for (int k = 0; k < nseg; ++k) m = fmaxf(m, seg_ml[k][g].x);
+      const float ms = (m == -INFINITY) ? 0.f : m;
+      const float old = fast_exp2(M[i] - ms);  // rescale what was folded so far
+      float l = L[i] * old, acc = A[i] * old;
+      for (int k = 0; k < nseg; ++k) {
+        const float f = fast_exp2(seg_ml[k][g].x - ms);
+        l = fmaf(seg_ml[k][g].y, f, l);
+        acc = fmaf(part_acc[((size_t)seg_part[k] * G + g) * D + d], f, acc);
+      }
+      M[i] = m; L[i] = l; A[i] = acc;
+    }
+    w = next_w; start = next_start; frac = next_frac;
+    __syncthreads();
+  }
+  for (int i = 0; i < per_thread; ++i) {
+    const int idx = tid + i * kBlock;
+    if (idx >= G * D) break;
+    const int g = idx / D, d = idx % D;
+    const float o = (L[i] > 0.f) ? A[i] / L[i] : 0.f;
+    store_row<E>(out + (row0 + g) * D + d, &o, 1);
+    if (lse && d == 0) lse[row0 + g] = (L[i] > 0.f) ? (M[i] + log2f(L[i])) * kLn2 : -INFINITY;
+  }
+}
+
+// Workgroups per compute unit of the balanced split: as many as fit, or a
+// fixed count when built with -DPKV_STREAM_BLOCKS_PER_CU=n (tuning).
+template <typename E, int D, int G>
+static int stream_blocks_per_cu() {
+#ifdef PKV_STREAM_BLOCKS_PER_CU
+  return PKV_STREAM_BLOCKS_PER_CU;
+#endif
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream_valu<E, D, G>, kBlock,
+                                                   0) != hipSuccess || nb < 1)
+    nb = 1;
+  return nb;
+}
+
+template <typename E, int D>
+static int blocks_by_group(int g) {
+  switch (g) {
+    case 1: return stream_blocks_per_cu<E, D, 1>();
+    case 2: return stream_blocks_per_cu<E, D, 2>();
+    case 4: return stream_blocks_per_cu<E, D, 4>();
+    case 8: return stream_blocks_per_cu<E, D, 8>();
+  }
+  return 1;
+}
+
+int stream_waves(int dtype, int head_dim, int group, int num_cus) {
+  static int cache[2][2][9] = {};  // [dtype][head_dim 64/128][group]: blocks per CU
+  int &bpc = cache[dtype == 1][head_dim == 128][group & 7 ? group : 8];
+  if (bpc == 0)
+    bpc = dtype == 1 ? (head_dim == 128 ? blocks_by_group<BF16, 128>(group)
+                                        : blocks_by_group<BF16, 64>(group))
+                     : (head_dim == 128 ? blocks_by_group<F32, 128>(group)
+                                        : blocks_by_group<F32, 64>(group));
+  return num_cus * bpc * kWaves;
+}
+
+template <typename E, int D, int G>
+static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t stream) {
+  const unsigned blocks = (unsigned)(nw / kWaves);
+  const size_t lds = sizeof(int) * ((size_t)a.batch + 1);
+  hipLaunchKernelGGL((decode_stream_valu<E, D, G>), dim3(blocks), dim3(kBlock), lds, stream,
+                     static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
+                     a.bank.num_pages, a.bank.num_kv_heads,
+                     static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
+                     a.pt_stride, a.seq_lens, a.batch, a.max_seq_len, a.scale * kLog2e,
+                     static_cast<typename E::storage *>(a.out), a.lse,
+                     reinterpret_cast<float2 *>(a.part_m), a.part_acc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_stream_combine<E, G>), dim3(a.batch * a.bank.num_kv_heads),
+                     dim3(kBlock), 0, stream, a.bank.num_kv_heads, D, a.seq_lens, a.batch,
+                     a.max_seq_len, nw, reinterpret_cast<const float2 *>(a.part_m), a.part_acc,
+                     static_cast<typename E::storage *>(a.out), a.lse);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t stream_by_group(const DecodeArgs &a, int64_t nw, hipStream_t stream) {
+  switch (a.num_q_heads / a.bank.num_kv_heads) {
+    case 1: return stream_launch<E, D, 1>(a, nw, stream);
+    case 2: return stream_launch<E, D, 2>(a, nw, stream);
+    case 4: return stream_launch<E, D, 4>(a, nw, stream);
+    case 8: return stream_launch<E, D, 8>(a, nw, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_stream(const DecodeArgs &a, int64_t nw, hipStream_t stream) {
+  if (a.bank.dtype == 1)
+    return a.bank.head_dim == 128 ? stream_by_group<BF16, 128>(a, nw, stream)
+                                  : stream_by_group<BF16, 64>(a, nw, stream);
+  return a.bank.head_dim == 128 ? stream_by_group<F32, 128>(a, nw, stream)
+                                : stream_by_group<F32, 64>(a, nw, stream);
+}
+
+}  // namespace pkv

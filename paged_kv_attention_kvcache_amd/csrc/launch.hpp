@@ -40,6 +40,12 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+// Balanced split ("stream-K"): nw waves take equal page ranges; part_m holds
+// float2 (m, l) per [wave][slot][head] and part_acc [wave][slot][head][D].
+hipError_t launch_decode_stream(const DecodeArgs &a, int64_t nw, hipStream_t stream);
+// Waves of the stream kernel that fit on num_cus compute units at once.
+int stream_waves(int dtype, int head_dim, int group, int num_cus);
+
 hipError_t launch_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads,
                          int32_t head_dim, const int32_t *seq_lens,
                          int32_t max_seq_len, int32_t partition,

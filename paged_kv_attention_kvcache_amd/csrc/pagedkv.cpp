@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 
 #include "launch.hpp"
@@ -28,8 +29,24 @@ int ok() {
   return PKV_OK;
 }
 
-constexpr int kDefaultPartition = 512;
+constexpr int kDefaultPartition = 512;  // fixed partitions when the balanced split is off
+constexpr int kStreamMaxBatch = 4096;   // rows the balanced split indexes in LDS
+constexpr int kWholeMaxSeq = 4096;      // longest context one workgroup reads whole
+constexpr int kWholeMinPairs = 512;     // (request, kv head) pairs that fill the GPU
 constexpr size_t kAlign = 256;
+
+enum class Mode { kWhole, kStream, kFixed };
+
+// partition 0: one workgroup per (request, kv head) reading its whole
+// context when there are enough pairs to fill the GPU and contexts are short
+// (no partials, no combine launch, and requests that share prefix pages read
+// them at about the same time); otherwise the balanced split. partition > 0:
+// fixed partitions of that many tokens.
+Mode decode_mode(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t partition) {
+  if (partition > 0) return Mode::kFixed;
+  if (max_seq_len <= kWholeMaxSeq && (int64_t)batch * hkv >= kWholeMinPairs) return Mode::kWhole;
+  return batch <= kStreamMaxBatch ? Mode::kStream : Mode::kFixed;
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -78,6 +95,37 @@ int check_heads(const pkv_pool *p, int32_t hq) {
   return PKV_OK;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Waves of the balanced split for this call: as many as are resident at once,
+// but no more than there are pages to stream (a multiple of 4).
+int64_t stream_wave_count(const pkv_pool *p, int32_t batch, int32_t hq, int32_t max_seq_len) {
+  const int g = hq / p->num_kv_heads;
+  int64_t nw = pkv::stream_waves(p->dtype, p->head_dim, g, device_cus());
+  const int64_t pages = (int64_t)batch * p->num_kv_heads * ((max_seq_len + 15) / 16);
+  nw = std::min<int64_t>(nw, (pages + 3) / 4 * 4);
+  return std::max<int64_t>(nw, 4);
+}
+
+// Tokens per workgroup in the fixed and whole modes.
+int32_t fixed_partition(Mode m, int32_t max_seq_len, int32_t partition) {
+  if (m == Mode::kWhole) return max_seq_len <= 16 ? 16 : (max_seq_len + 15) / 16 * 16;
+  return partition > 0 ? partition : kDefaultPartition;
+}
+
 int launched(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(PKV_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -124,15 +172,23 @@ int paged_kv_write(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, con
                   "paged_kv_write");
 }
 
-size_t paged_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+size_t paged_decode_workspace_bytes(const pkv_pool *pool, int32_t batch, int32_t num_q_heads,
                                     int32_t max_seq_len, int32_t partition) {
-  if (partition == 0) partition = kDefaultPartition;
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition <= 0)
+  if (!pool || batch <= 0 || num_q_heads <= 0 || pool->num_kv_heads <= 0 ||
+      num_q_heads % pool->num_kv_heads != 0 || pool->head_dim <= 0 || max_seq_len < 0 ||
+      partition < 0)
     return 0;
+  const size_t D = (size_t)pool->head_dim;
+  const Mode mode = decode_mode(batch, pool->num_kv_heads, max_seq_len, partition);
+  if (mode == Mode::kStream) {
+    const size_t slots = (size_t)stream_wave_count(pool, batch, num_q_heads, max_seq_len) * 2 *
+                         (num_q_heads / pool->num_kv_heads);
+    return align_up(slots * 2 * sizeof(float)) + align_up(slots * D * sizeof(float));
+  }
+  partition = fixed_partition(mode, max_seq_len, partition);
   const size_t parts = max_seq_len > 0 ? (size_t)(max_seq_len + partition - 1) / partition : 1;
   const size_t rows = (size_t)batch * num_q_heads;
-  return 2 * align_up(rows * parts * sizeof(float)) +
-         align_up(rows * parts * head_dim * sizeof(float));
+  return 2 * align_up(rows * parts * sizeof(float)) + align_up(rows * parts * D * sizeof(float));
 }
 
 int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
@@ -152,14 +208,17 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, 
   if (max_seq_len < 0 || (int64_t)max_seq_len > (int64_t)page_table_stride * pool->page_size)
     return fail(PKV_EINVAL, "max_seq_len %d outside [0, stride * page_size = %lld]", max_seq_len,
                 (long long)page_table_stride * pool->page_size);
-  if (partition == 0) partition = kDefaultPartition;
   if (partition < 0 || partition % 16 != 0)
-    return fail(PKV_EINVAL, "partition %d must be a positive multiple of 16", partition);
-  const size_t need = paged_decode_workspace_bytes(batch, num_q_heads, pool->head_dim,
-                                                   max_seq_len, partition);
-  const int32_t max_parts = max_seq_len > 0 ? (max_seq_len + partition - 1) / partition : 1;
-  if (max_parts > 1 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EINVAL, "partition %d must be 0 or a positive multiple of 16", partition);
+  const size_t need = paged_decode_workspace_bytes(pool, batch, num_q_heads, max_seq_len,
+                                                   partition);
+  if (!workspace || workspace_bytes < need)
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  const Mode mode = decode_mode(batch, pool->num_kv_heads, max_seq_len, partition);
+  const bool stream_mode = mode == Mode::kStream;
+  if (!stream_mode) partition = fixed_partition(mode, max_seq_len, partition);
+  const int32_t max_parts =
+      stream_mode || max_seq_len == 0 ? 1 : (max_seq_len + partition - 1) / partition;
   if (max_parts > 65535) return fail(PKV_EINVAL, "too many partitions (%d)", max_parts);
 
   pkv::DecodeArgs a{};
@@ -176,13 +235,20 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, 
   a.max_parts = max_parts;
   a.out = out;
   a.lse = lse;
-  if (workspace) {
-    const size_t rows = (size_t)batch * num_q_heads;
-    char *ws = static_cast<char *>(workspace);
+  char *ws = static_cast<char *>(workspace);
+  if (stream_mode) {
+    const int64_t nw = stream_wave_count(pool, batch, num_q_heads, max_seq_len);
+    const size_t slots = (size_t)nw * 2 * (num_q_heads / pool->num_kv_heads);
     a.part_m = reinterpret_cast<float *>(ws);
-    a.part_l = reinterpret_cast<float *>(ws + align_up(rows * max_parts * sizeof(float)));
-    a.part_acc = reinterpret_cast<float *>(ws + 2 * align_up(rows * max_parts * sizeof(float)));
+    a.part_acc = reinterpret_cast<float *>(ws + align_up(slots * 2 * sizeof(float)));
+    return launched(pkv::launch_decode_stream(a, nw, static_cast<hipStream_t>(stream)),
+                    "paged_decode_attn");
   }
+  const size_t rows = (size_t)batch * num_q_heads;
+  const size_t ml = align_up(rows * max_parts * sizeof(float));
+  a.part_m = reinterpret_cast<float *>(ws);
+  a.part_l = reinterpret_cast<float *>(ws + ml);
+  a.part_acc = reinterpret_cast<float *>(ws + 2 * ml);
   return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), "paged_decode_attn");
 }
 

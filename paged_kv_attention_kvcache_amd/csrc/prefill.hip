@@ -36,10 +36,10 @@ __global__ __launch_bounds__(kBlock) void prefill_valu(
   const int pos = min(n - qlen + (row - cu_q_lens[r]), n - 1);
   const int hi = max(pos + 1, 0);
 
-  float qv[G][TL::kVecN];
-  load_q<E, D, G>(q + ((size_t)row * hq + (size_t)kvh * G) * D, qscale, qv);
+  QChunk<E> qv[G];
+  load_q<E, D, G>(q + ((size_t)row * hq + (size_t)kvh * G) * D, qv);
   valu_span<E, D, G>(kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, 0, hi, qv,
-                     lds_ml, lds_acc);
+                     qscale, lds_ml, lds_acc);
 
   for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
     const int g = idx / D, d = idx % D;

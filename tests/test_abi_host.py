@@ -69,13 +69,17 @@ def test_bank_map_rejects(L):
 
 
 def test_workspace_bytes(L):
-    # rows * parts floats for m and l, rows * parts * D for acc, 256-aligned
+    # fixed partitions: rows * parts floats for m and l, rows * parts * D for
+    # acc, each 256-aligned
+    st, keep = _pool(kv=2)
     rows, parts, D = 3 * 8, 4, 128
-    need = L.paged_decode_workspace_bytes(3, 8, D, 2048, 512)
+    need = L.paged_decode_workspace_bytes(ctypes.byref(st), 3, 8, 2048, 512)
     al = lambda x: (x + 255) // 256 * 256
     assert need == 2 * al(rows * parts * 4) + al(rows * parts * D * 4)
-    assert L.paged_decode_workspace_bytes(3, 8, D, 2048, 0) == need  # default 512
-    assert L.paged_decode_workspace_bytes(0, 8, D, 2048, 512) == 0
+    # balanced split: two (m, l, acc) slots per wave and head of the group
+    assert L.paged_decode_workspace_bytes(ctypes.byref(st), 3, 8, 2048, 0) > 0
+    assert L.paged_decode_workspace_bytes(ctypes.byref(st), 0, 8, 2048, 512) == 0
+    assert L.paged_decode_workspace_bytes(ctypes.byref(st), 3, 7, 2048, 512) == 0
 
 
 def _pool(dtype=1, page_size=16, head_dim=128, planes=2, layers=3, rec=(0, 3), kv=2,
@@ -126,6 +130,7 @@ def test_decode_validation(L):
     assert call(part=24) == pkv.PKV_EINVAL        # not a multiple of 16
     assert call(max_seq=64, part=16) == pkv.PKV_EWORKSPACE
     assert call(max_seq=64, part=16, ws=FAKE, ws_bytes=16) == pkv.PKV_EWORKSPACE
+    assert call(max_seq=64, part=0, ws=FAKE, ws_bytes=16) == pkv.PKV_EWORKSPACE
     assert "workspace" in pkv.last_error()
 
 

@@ -143,7 +143,7 @@ def test_decode_parity(name, seed):
             check(f"{name}/s{seed}/q{q_scale}/p{partition}", case.layout.dtype, out, ro, rl, lse)
 
 
-@pytest.mark.parametrize("partition", [16, 32, 512])
+@pytest.mark.parametrize("partition", [0, 16, 32, 512])
 def test_decode_edge_lengths(partition):
     # seq_len 0 (empty row), 1, page and partition boundaries, a ragged tail
     lens = [0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000]
