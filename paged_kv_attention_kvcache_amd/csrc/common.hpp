@@ -23,14 +23,6 @@ struct BF16 {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // 16 bytes -> fp32 values (8 for bf16, 4 for fp32).
 template <typename E> struct Vec;
 template <> struct Vec<BF16> {
@@ -82,13 +74,36 @@ template <> struct QChunk<F32> {
   }
 };
 
-// Store n fp32 values as the storage type (n = 8 for bf16 -> 16 bytes).
+// Store n fp32 values as the storage type (bf16 by the hardware's
+// round-to-nearest-even conversion). n a multiple of 8 (bf16) or 4 (fp32)
+// with a 16-byte aligned destination uses 16-byte stores.
 template <typename E> __device__ __forceinline__ void store_row(typename E::storage *dst, const float *v, int n);
 template <> __device__ __forceinline__ void store_row<F32>(float *dst, const float *v, int n) {
-  for (int i = 0; i < n; ++i) dst[i] = v[i];
+  if ((n & 3) == 0) {
+    for (int i = 0; i < n; i += 4)
+      *reinterpret_cast<float4 *>(dst + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+  } else {
+    for (int i = 0; i < n; ++i) dst[i] = v[i];
+  }
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, p);
 }
 template <> __device__ __forceinline__ void store_row<BF16>(uint16_t *dst, const float *v, int n) {
-  for (int i = 0; i < n; ++i) dst[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+  if ((n & 7) == 0) {
+    for (int i = 0; i < n; i += 8) {
+      uint4 w;
+      w.x = pack_bf16x2(v[i], v[i + 1]);
+      w.y = pack_bf16x2(v[i + 2], v[i + 3]);
+      w.z = pack_bf16x2(v[i + 4], v[i + 5]);
+      w.w = pack_bf16x2(v[i + 6], v[i + 7]);
+      *reinterpret_cast<uint4 *>(dst + i) = w;
+    }
+  } else {
+    for (int i = 0; i < n; ++i) dst[i] = (uint16_t)(pack_bf16x2(v[i], 0.f) & 0xffffu);
+  }
 }
 
 template <int CTRL> __device__ __forceinline__ float dpp(float x) {

@@ -1,5 +1,5 @@
-// Split-K paged decode attention for gfx950: partial kernel + fixed-order
-// combine kernel.
+// Split-K paged decode attention for gfx950 with fixed partitions: partial
+// kernel + fixed-order combine kernel.
 //
 // One query per request sits at position seq_len - 1 and reads the whole
 // context through the page table ("Faster fuzzy minds", sections "When
@@ -11,8 +11,8 @@
 // them in partition order (deterministic). Rows whose context fits one
 // partition are finished directly by the partial kernel, and the combine
 // kernel is launched only when some row can span several partitions.
+#include "folds.hpp"
 #include "launch.hpp"
-#include "valu_span.hpp"
 
 namespace pkv {
 
@@ -36,24 +36,17 @@ __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
   }
 }
 
-template <typename E>
-__device__ __forceinline__ void finish(typename E::storage *__restrict__ out,
-                                       float *__restrict__ lse, size_t rowh, int D, int d,
-                                       float M, float L, float A) {
-  const float o = (L > 0.f) ? A / L : 0.f;
-  store_row<E>(out + rowh * D + d, &o, 1);
-  if (lse && d == 0) lse[rowh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
-}
-
-template <typename E, int D, int G>
-__global__ __launch_bounds__(kBlock) void decode_partial_valu(
+// One workgroup per (partition j, kv head, request): the 4 waves take pages
+// w, w+4, ... of the partition, their states meet in LDS.
+template <typename E, class F>
+__global__ __launch_bounds__(kBlock) void decode_block(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
     const typename E::storage *__restrict__ q, int32_t hq,
     const int32_t *__restrict__ page_table, int32_t pt_stride,
     const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale, int32_t partition,
     int32_t max_parts, typename E::storage *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc) {
-  using TL = Tile<E, D>;
+  constexpr int G = F::kGroup, D = F::kHeadDim;
   __shared__ float2 lds_ml[kWaves * G];
   __shared__ float lds_acc[kWaves * G * D];
 
@@ -64,10 +57,19 @@ __global__ __launch_bounds__(kBlock) void decode_partial_valu(
   if (j > 0 && j >= np) return;  // partition past the context (whole block exits)
   const int hi = min(lo + partition, n);
 
-  QChunk<E> qv[G];
-  load_q<E, D, G>(q + ((size_t)r * hq + (size_t)kvh * G) * D, qv);
-  valu_span<E, D, G>(kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, lo, hi,
-                     qv, qscale, lds_ml, lds_acc);
+  F f(q + ((size_t)r * hq + (size_t)kvh * G) * D, qscale);
+  typename F::State st;
+  f.reset(st);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p_first = lo / kPage;
+  const int n_pages = hi > lo ? (hi - 1) / kPage - p_first + 1 : 0;
+  const int npw = n_pages > w ? (n_pages - w + kWaves - 1) / kWaves : 0;
+  if (npw > 0)
+    stream_pages(f, st, kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh,
+                 p_first + w, npw, kWaves, lo, hi);
+  f.finish_wave(st);
+  emit_to_lds(f, st, w, lds_ml, lds_acc);
+  __syncthreads();
 
   const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
   if (np <= 1) {  // the whole context in one partition: finish here
@@ -113,8 +115,9 @@ __global__ __launch_bounds__(128) void decode_reduce(
 
 template <typename E, int D, int G>
 static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
+  using F = typename FoldFor<E, D, G>::type;
   const dim3 grid(a.max_parts, a.bank.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((decode_partial_valu<E, D, G>), grid, dim3(kBlock), 0, stream,
+  hipLaunchKernelGGL((decode_block<E, F>), grid, dim3(kBlock), 0, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads,
                      static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,

@@ -13,8 +13,8 @@
 // position order. The split depends only on the sequence lengths and the
 // grid size, so results are bitwise repeatable and independent of where the
 // pages live.
+#include "folds.hpp"
 #include "launch.hpp"
-#include "valu_span.hpp"
 
 namespace pkv {
 
@@ -66,21 +66,18 @@ __device__ __forceinline__ size_t part_index(int64_t wave, int slot, int G, int 
   return ((size_t)wave * 2 + slot) * G + g;
 }
 
-template <typename E, int D, int G>
-__global__ __launch_bounds__(kBlock) void decode_stream_valu(
+template <typename E, class F>
+__global__ __launch_bounds__(kBlock) void decode_stream(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
     const typename E::storage *__restrict__ q, int32_t hq,
     const int32_t *__restrict__ page_table, int32_t pt_stride,
     const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
     typename E::storage *__restrict__ out, float *__restrict__ lse,
     float2 *__restrict__ part_ml, float *__restrict__ part_acc) {
-  using TL = Tile<E, D>;
-  constexpr int N = TL::kVecN, LPT = TL::kLPT;
+  constexpr int G = F::kGroup, D = F::kHeadDim;
   extern __shared__ int cum[];  // [batch + 1]
   row_prefix(seq_lens, batch, max_seq_len, hkv, cum);
 
-  const int lane = threadIdx.x & 63;
-  const int row = lane / LPT, c = lane % LPT;
   const int64_t nw = (int64_t)gridDim.x * kWaves;
   const int64_t gw = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t total = cum[batch];
@@ -102,35 +99,23 @@ __global__ __launch_bounds__(kBlock) void decode_stream_valu(
   while (s < e) {
     const int len = (int)min((int64_t)(pr - p), e - s);
     const int n = min(max(seq_lens[r], 0), max_seq_len);
-    QChunk<E> qv[G];
-    load_q<E, D, G>(q + ((size_t)r * hq + (size_t)kvh * G) * D, qv);
-    SpanState<E, D, G> st;
-    reset(st);
-    wave_span<E, D, G>(st, kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, p,
-                       len, 1, 0, n, qv, qscale);
-    merge_rows(st);
-    if (row == 0) {
-      const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
-      if (p == 0 && len == pr) {  // the whole unit: finish here
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float inv = st.l[g] > 0.f ? 1.f / st.l[g] : 0.f;
-          float o[N];
-#pragma unroll
-          for (int e2 = 0; e2 < N; ++e2) o[e2] = st.acc[g][e2] * inv;
-          store_row<E>(out + (row0 + g) * D + c * N, o, N);
-          if (lse && c == 0)
-            lse[row0 + g] = st.l[g] > 0.f ? (st.m[g] + log2f(st.l[g])) * kLn2 : -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const size_t pi = part_index(gw, slot, G, g);
-#pragma unroll
-          for (int e2 = 0; e2 < N; ++e2) part_acc[pi * D + c * N + e2] = st.acc[g][e2];
-          if (c == 0) part_ml[pi] = make_float2(st.m[g], st.l[g]);
-        }
-      }
+    const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
+    F f(q + row0 * D, qscale);
+    typename F::State st;
+    f.reset(st);
+    stream_pages(f, st, kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, p, len,
+                 1, 0, n);
+    f.finish_wave(st);
+    if (p == 0 && len == pr) {  // the whole unit: finish here
+      emit_final<F, E>(f, st, out, lse, row0);
+    } else {
+      f.emit(st, [&](int g, int d0, int cnt, float m, float l, const float *acc) {
+        const size_t pi = part_index(gw, slot, G, g);
+        for (int e2 = 0; e2 < cnt; e2 += 4)
+          *reinterpret_cast<float4 *>(part_acc + pi * D + d0 + e2) =
+              make_float4(acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]);
+        if (d0 == 0) part_ml[pi] = make_float2(m, l);
+      });
     }
     s += len;
     slot = 1;
@@ -259,7 +244,7 @@ static int stream_blocks_per_cu() {
   return PKV_STREAM_BLOCKS_PER_CU;
 #endif
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream_valu<E, D, G>, kBlock,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_stream<E, typename FoldFor<E, D, G>::type>, kBlock,
                                                    0) != hipSuccess || nb < 1)
     nb = 1;
   return nb;
@@ -291,7 +276,7 @@ template <typename E, int D, int G>
 static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t stream) {
   const unsigned blocks = (unsigned)(nw / kWaves);
   const size_t lds = sizeof(int) * ((size_t)a.batch + 1);
-  hipLaunchKernelGGL((decode_stream_valu<E, D, G>), dim3(blocks), dim3(kBlock), lds, stream,
+  hipLaunchKernelGGL((decode_stream<E, typename FoldFor<E, D, G>::type>), dim3(blocks), dim3(kBlock), lds, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads,
                      static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,

@@ -1,0 +1,175 @@
+// Vector-ALU fold of paged K/V tiles for a GQA group of G query heads.
+//
+// Used where the contraction is too skinny for matrix cores (a group of 1 or
+// 2 query heads, fp32 data, or head_dim 64). Within a wave, LPT =
+// head_dim*bytes/16 consecutive lanes hold one token row of a (page, kv head)
+// tile, 16 bytes each, so every load instruction of a wave reads 1 KiB of
+// the 4 KiB tile contiguously. A q.k dot product is an in-lane chain (packed
+// v_dot2_f32_bf16 for bf16, FMAs for fp32) plus a DPP butterfly over the LPT
+// lanes of the row; each row then keeps its own online-softmax state (m, l,
+// acc) over the tokens it sees, so no cross-row traffic happens inside the
+// page loop. finish_wave() merges the rows with lane shuffles in a fixed
+// order (bitwise repeatable, independent of physical page ids).
+//
+// Scores are in base-2 units: each reduced q.k is multiplied by
+// scale*log2(e) and the softmax uses exp2.
+#pragma once
+#include "span.hpp"
+
+namespace pkv {
+
+template <typename E, int D> struct Tile {
+  static constexpr int kVecN = Vec<E>::kN;       // elements per 16-byte chunk
+  static constexpr int kLPT = D / kVecN;         // lanes per token row
+  static constexpr int kRPW = 64 / kLPT;         // token rows per wave load
+  static constexpr int kNI = kPage / kRPW;       // wave loads per tile
+  static constexpr int kTileVec = kPage * kLPT;  // 16-byte chunks per tile
+  static_assert(kLPT == 8 || kLPT == 16 || kLPT == 32, "unsupported head_dim");
+};
+
+template <typename E, int D, int G>
+struct ValuFold {
+  using TL = Tile<E, D>;
+  static constexpr int N = TL::kVecN, LPT = TL::kLPT, RPW = TL::kRPW, NI = TL::kNI;
+  static constexpr int kPagesPerStep = 1;
+  static constexpr int kGroup = G;
+  static constexpr int kHeadDim = D;
+
+  struct State {
+    float m[G], l[G], acc[G][N];
+  };
+  struct Regs {
+    uint4 k[NI], v[NI];
+  };
+
+  QChunk<E> q[G];
+  float qscale;
+  int row, c;
+  uint32_t lane_off;  // bytes into a tile
+
+  // qrow: the first of the G query rows (contiguous, head_dim each).
+  __device__ __forceinline__ ValuFold(const typename E::storage *__restrict__ qrow, float qs)
+      : qscale(qs) {
+    const int lane = threadIdx.x & 63;
+    row = lane / LPT;
+    c = lane % LPT;
+    lane_off = (uint32_t)(row * LPT + c) * 16u;
+    const uint4 *qv = reinterpret_cast<const uint4 *>(qrow);
+#pragma unroll
+    for (int g = 0; g < G; ++g) q[g].set(qv[g * LPT + c]);
+  }
+
+  __device__ __forceinline__ void reset(State &st) const {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      st.m[g] = -INFINITY;
+      st.l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < N; ++e) st.acc[g][e] = 0.f;
+    }
+  }
+
+  // The (page, kv head) tile rows this lane owns; page and kvh are
+  // wave-uniform, so the tile base is a scalar address.
+  __device__ __forceinline__ void load(Regs &r, const uint4 *__restrict__ kb,
+                                       const uint4 *__restrict__ vb, int page, int,
+                                       int hkv, int kvh) const {
+    const size_t tile = ((size_t)page * hkv + kvh) * TL::kTileVec;
+    const char *kt = reinterpret_cast<const char *>(kb + tile);
+    const char *vt = reinterpret_cast<const char *>(vb + tile);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) r.k[i] = load_stream(kt + lane_off + i * RPW * LPT * 16u);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) r.v[i] = load_stream(vt + lane_off + i * RPW * LPT * 16u);
+  }
+
+  // Folds page pi of the request (keys outside [lo, hi) masked).
+  __device__ __forceinline__ void fold(State &st, const Regs &r, int pi, int, int lo,
+                                       int hi) const {
+    const int pos0 = pi * kPage + row;  // token of load i: pos0 + i * RPW
+    const bool full = (pi * kPage >= lo) && (pi * kPage + kPage <= hi);
+    float s[G][NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g][i] = q[g].dot(r.k[i]);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) s[g][i] = group_sum<LPT>(s[g][i]) * qscale;
+    bool valid[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = pos0 + i * RPW;
+      valid[i] = full || (pos >= lo && pos < hi);
+      if (!valid[i]) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[g][i] = -INFINITY;
+      }
+    }
+    // One rescale per page and head, then the V rows one at a time (a masked
+    // row is replaced by zeros so that poison in unused slots cannot leak).
+    float ms[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mx = s[g][0];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[g][i]);
+      const float mn = fmaxf(st.m[g], mx);
+      ms[g] = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(st.m[g] - ms[g]);
+      st.l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < N; ++e) st.acc[g][e] *= alpha;
+      st.m[g] = mn;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[N];
+      Vec<E>::widen(r.v[i], vf);
+      if (!valid[i]) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = fast_exp2(s[g][i] - ms[g]);
+        st.l[g] += p;
+#pragma unroll
+        for (int e = 0; e < N; ++e) st.acc[g][e] = fmaf(p, vf[e], st.acc[g][e]);
+      }
+    }
+  }
+
+  // Merge the RPW row states (rows sit LPT lanes apart) with a fixed
+  // butterfly; afterwards the lanes of row 0 hold the wave's state.
+  __device__ __forceinline__ void finish_wave(State &st) const {
+#pragma unroll
+    for (int mask = LPT; mask < 64; mask <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = __shfl_xor(st.m[g], mask);
+        const float lo_ = __shfl_xor(st.l[g], mask);
+        const float mn = fmaxf(st.m[g], mo);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        const float a = fast_exp2(st.m[g] - ms), b = fast_exp2(mo - ms);
+        st.l[g] = st.l[g] * a + lo_ * b;
+#pragma unroll
+        for (int e = 0; e < N; ++e) {
+          const float ao = __shfl_xor(st.acc[g][e], mask);
+          st.acc[g][e] = st.acc[g][e] * a + ao * b;
+        }
+        st.m[g] = mn;
+      }
+    }
+  }
+
+  template <class Fn>
+  __device__ __forceinline__ void emit(const State &st, Fn &&fn) const {
+    if (row != 0) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g) fn(g, c * N, N, st.m[g], st.l[g], st.acc[g]);
+  }
+};
+
+}  // namespace pkv

@@ -7,8 +7,8 @@
 // position. One workgroup takes one (query row, kv head) and the whole GQA
 // group of query heads, streaming its visible pages with the same span code
 // as decode.
+#include "fold_valu.hpp"
 #include "launch.hpp"
-#include "valu_span.hpp"
 
 namespace pkv {
 
@@ -19,7 +19,6 @@ __global__ __launch_bounds__(kBlock) void prefill_valu(
     int32_t batch, const int32_t *__restrict__ page_table, int32_t pt_stride,
     const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale,
     typename E::storage *__restrict__ out, float *__restrict__ lse) {
-  using TL = Tile<E, D>;
   __shared__ float2 lds_ml[kWaves * G];
   __shared__ float lds_acc[kWaves * G * D];
 
@@ -36,19 +35,24 @@ __global__ __launch_bounds__(kBlock) void prefill_valu(
   const int pos = min(n - qlen + (row - cu_q_lens[r]), n - 1);
   const int hi = max(pos + 1, 0);
 
-  QChunk<E> qv[G];
-  load_q<E, D, G>(q + ((size_t)row * hq + (size_t)kvh * G) * D, qv);
-  valu_span<E, D, G>(kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, 0, hi, qv,
-                     qscale, lds_ml, lds_acc);
+  ValuFold<E, D, G> f(q + ((size_t)row * hq + (size_t)kvh * G) * D, qscale);
+  typename ValuFold<E, D, G>::State st;
+  f.reset(st);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_pages = hi > 0 ? (hi - 1) / kPage + 1 : 0;
+  const int npw = n_pages > w ? (n_pages - w + kWaves - 1) / kWaves : 0;
+  if (npw > 0)
+    stream_pages(f, st, kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, w, npw,
+                 kWaves, 0, hi);
+  f.finish_wave(st);
+  emit_to_lds(f, st, w, lds_ml, lds_acc);
+  __syncthreads();
 
   for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
     const int g = idx / D, d = idx % D;
     float M, L, A;
     combine_waves<G, D>(lds_ml, lds_acc, g, d, M, L, A);
-    const size_t rowh = (size_t)row * hq + (size_t)kvh * G + g;
-    const float o = (L > 0.f) ? A / L : 0.f;
-    store_row<E>(out + rowh * D + d, &o, 1);
-    if (lse && d == 0) lse[rowh] = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+    finish<E>(out, lse, (size_t)row * hq + (size_t)kvh * G + g, D, d, M, L, A);
   }
 }
 

@@ -127,6 +127,9 @@ DECODE_CASES = {
                         num_kv_heads=2, head_dim=128),
     "f32_d64_g8": dict(dtype="f32", batch=3, seq_range=(30, 1100), num_q_heads=8,
                        num_kv_heads=1, head_dim=64),
+    # matrix-core fold, group 4, ragged lengths incl. odd page counts
+    "bf16_d128_g4": dict(dtype="bf16", batch=7, seq_range=(1, 1500), num_q_heads=16,
+                         num_kv_heads=4, head_dim=128),
 }
 
 
