@@ -2,9 +2,10 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
 A step is one decode step of a looped model through every (plane, layer) bank
-in model order: for each bank, store_kv writes each request's newest token
-(paged_kv_write), then decode attention reads the whole context through the
-page table (paged_decode_attn: split-K partials, combined by the last workgroup).
+in model order: for each bank, store_kv writes each request's newest token and
+decode attention reads the whole context through the page table. By default
+both happen in one call (paged_decode_append_attn); --separate-write issues
+paged_kv_write then paged_decode_attn instead (same results, bit for bit).
 
 Default workload (Ouro-style fixed depth): 24 layers x 4 loop planes = 96
 banks, batch 64, seq_lens uniform in [512, 2048], page size 16, 16 query / 8
@@ -20,7 +21,6 @@ inputs resident in HBM before the timed region starts.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -41,19 +41,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "paged_kv_attention_kvcache_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profiles(workload: str, launches_per_unit: float = 1.0):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary, or None when it was taken on different kernel sources."""
+    from paged_kv_attention_kvcache_amd.rocprof_summary import kernel_source_hash
+
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -115,6 +107,14 @@ class DecodeWorkload:
         wsb = pkv.workspace_bytes(self.pool, batch, hq, self.max_seq, self.partition)
         self.ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
         self.pkv = pkv
+        self.separate_write = False
+        self.split = pkv.split_mode(self.pool, batch, hq, self.max_seq, self.partition)
+        g = hq // hkv
+        fold = f"MfmaFold<{g}>" if g in (4, 8) and D == 128 else f"ValuFold<BF16, {D}, {g}>"
+        self.kernel_name = {
+            "whole": f"decode_block<BF16, {fold}> (one launch per call)",
+            "balanced": f"decode_stream<BF16, {fold}> + decode_stream_combine",
+            "fixed": f"decode_block<BF16, {fold}> + decode_reduce"}[self.split]
         # algorithmic bytes: each request reads its whole context (K and V)
         self.kv_bytes_per_call = int(self.seq.astype(np.int64).sum()) * 2 * hkv * D * 2
         uniq_pages = len(np.unique(np.concatenate(
@@ -129,16 +129,18 @@ class DecodeWorkload:
             hb = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
             self.snap.append((hb(k[b])[None], hb(v[b])[None], hb(self.q[i])))
 
-    def call(self, i, timing=None):
+    def call(self, i, decode_only=False):
         plane, layer = self.order[i]
         pkv = self.pkv
-        pkv.kv_write(self.pool, plane, layer, self.nk[i], self.nv[i], self.slots)
-        if timing is not None:
-            timing[0].record()
+        if self.separate_write:
+            if not decode_only:
+                pkv.kv_write(self.pool, plane, layer, self.nk[i], self.nv[i], self.slots)
+            extra = {}
+        else:
+            extra = dict(k_new=self.nk[i], v_new=self.nv[i])
         pkv.decode(self.pool, plane, layer, self.q[i], self.table_d, self.seq_d, self.max_seq,
-                   partition=self.partition, out=self.out, lse=self.lse, workspace=self.ws)
-        if timing is not None:
-            timing[1].record()
+                   partition=self.partition, out=self.out, lse=self.lse, workspace=self.ws,
+                   **extra)
 
     def step(self):
         for i in range(len(self.order)):
@@ -174,6 +176,121 @@ CONFIG_TEXT = {
 }
 
 
+# --------------------------------------------------------------------------- prefill
+
+class PrefillWorkload:
+    """Chunked causal prefill: `prompts` prompts of `n` tokens, 32 MHA heads,
+    head_dim 128, bf16, page size 16, written then attended chunk by chunk
+    (paged_kv_write + paged_prefill_attn per chunk). Calls rotate over `banks`
+    banks of one pool so that each call's K/V come from HBM, not cache."""
+
+    def __init__(self, prompts=8, n=512, heads=32, D=128, banks=132, seed=0):
+        import torch
+
+        import paged_kv_attention_kvcache_amd as pkv
+        from paged_kv_attention_kvcache_amd import synth
+
+        self.pkv, self.n, self.prompts, self.heads, self.D = pkv, n, prompts, heads, D
+        rng = np.random.default_rng(seed)
+        lens = np.full(prompts, n, np.int32)
+        self.table, self.num_pages, _ = synth.allocate_pages(rng, lens, 16)
+        self.bank_of, self.nb = pkv.bank_map(banks, 1)
+        shape = (self.nb, self.num_pages, heads, 16, D)
+        k = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), seed + 1)
+        v = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), seed + 2)
+        self.pool = pkv.Pool(torch.bfloat16, self.num_pages, heads, D, self.bank_of, self.nb,
+                             k=k, v=v)
+        tokens = prompts * n
+        self.q = synth.device_normal_(torch.empty((tokens, heads, D), dtype=torch.bfloat16,
+                                                  device="cuda"), seed + 3)
+        self.kn = synth.device_normal_(torch.empty((tokens, heads, D), dtype=torch.bfloat16,
+                                                   device="cuda"), seed + 4)
+        self.vn = synth.device_normal_(torch.empty((tokens, heads, D), dtype=torch.bfloat16,
+                                                   device="cuda"), seed + 5)
+        self.out = torch.empty_like(self.q)
+        self.table_d = torch.from_numpy(self.table).cuda()
+        self.synth = synth
+
+    def schedule(self, chunk, start=0):
+        """Per chunk: (slots, cu_q_lens, seq_lens, first row, rows, visible pairs)."""
+        import torch
+
+        out, lo = [], start
+        while lo < self.n:
+            hi = min(lo + chunk, self.n)
+            q_len = hi - lo
+            slots = np.concatenate([self.synth.slots_of(self.table, r, np.arange(lo, hi), 16)
+                                    for r in range(self.prompts)])
+            rows = np.concatenate([r * self.n + np.arange(lo, hi) for r in range(self.prompts)])
+            pairs = self.prompts * sum(p + 1 for p in range(lo, hi))
+            out.append(dict(slots=torch.from_numpy(slots).cuda(),
+                            rows=torch.from_numpy(rows.astype(np.int64)).cuda(),
+                            cu=torch.from_numpy(np.arange(0, self.prompts + 1, dtype=np.int32)
+                                                * q_len).cuda(),
+                            seq=torch.from_numpy(np.full(self.prompts, hi, np.int32)).cuda(),
+                            q_len=q_len, hi=hi, pairs=pairs))
+            lo = hi
+        for c in out:  # gathered per chunk so the timed calls read packed inputs
+            c["q"] = self.q[c["rows"]].contiguous()
+            c["k"] = self.kn[c["rows"]].contiguous()
+            c["v"] = self.vn[c["rows"]].contiguous()
+            c["o"] = torch.empty_like(c["q"])
+        return out
+
+    def run(self, chunks, bank, write=True):
+        pkv = self.pkv
+        for c in chunks:
+            if write:
+                pkv.kv_write(self.pool, bank, 0, c["k"], c["v"], c["slots"])
+            pkv.prefill(self.pool, bank, 0, c["q"], c["cu"], self.table_d, c["seq"], c["q_len"],
+                        c["hi"], out=c["o"], with_lse=False)
+
+
+def run_prefill(reps=3, supplementary=True):
+    """TFLOP/s of causal prefill: 4 * head_dim * heads * (visible query-key
+    pairs) algorithmic flops per call, written then attended."""
+    import torch
+
+    res = {}
+    cases = [("cold_chunk2048", 8, 512, 2048, 0), ("cold_chunk128", 8, 512, 128, 0),
+             ("suffix16_over_496", 8, 512, 4096, 496)]
+    if supplementary:
+        cases.append(("cold_2048x8_chunk2048", 8, 2048, 2048, 0))
+    wls = {}
+    for name, prompts, n, chunk, start in cases:
+        if (prompts, n) not in wls:
+            wls[(prompts, n)] = PrefillWorkload(prompts, n, banks=132 if n <= 512 else 24)
+        wl = wls[(prompts, n)]
+        chunks = wl.schedule(chunk, start)
+        if start:  # the cached prefix is already in every bank (from the generator)
+            pass
+        flops = 4 * wl.D * wl.heads * sum(c["pairs"] for c in chunks)
+        hbm = sum(c["hi"] * wl.prompts * 2 * wl.heads * wl.D * 2 + 2 * c["q"].numel() * 2
+                  for c in chunks)
+        for b in range(2):
+            wl.run(chunks, b)
+        torch.cuda.synchronize()
+        out = {}
+        for write in (True, False):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            nbk = wl.nb
+            a.record()
+            for i in range(reps * nbk):
+                wl.run(chunks, i % nbk, write=write)
+            e.record()
+            torch.cuda.synchronize()
+            sec = a.elapsed_time(e) / 1e3 / (reps * nbk)
+            key = "write_then_attend" if write else "attend_only"
+            out[key] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 2),
+                        "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "hbm_GBps": round(hbm / sec / 1e9, 1)}
+        out["flops"] = flops
+        out["algorithmic_bytes"] = hbm
+        res[name] = out
+        log(f"prefill {name}: {out}")
+    return res
+
+
 # --------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(wl: DecodeWorkload, budget_s: float = 15.0):
@@ -187,19 +304,22 @@ def cpu_baseline(wl: DecodeWorkload, budget_s: float = 15.0):
     cores = int(os.environ["OMP_NUM_THREADS"])
     done_bytes, spent, calls = 0, 0.0, 0
     bank_of = np.zeros((1, 1), np.int32)
-    for k, v, q in wl.snap:
-        op = oracle.Pool("bf16", 16, wl.num_pages, wl.hkv, wl.D, bank_of, 1, k, v)
-        t0 = time.perf_counter()
-        oracle.decode(op, 0, 0, q, wl.table, wl.seq)
-        spent += time.perf_counter() - t0
-        done_bytes += wl.kv_bytes_per_call
-        calls += 1
-        if spent >= budget_s:
-            break
+    pools = [(oracle.Pool("bf16", 16, wl.num_pages, wl.hkv, wl.D, bank_of, 1, k, v), q)
+             for k, v, q in wl.snap]
+    while pools and spent < budget_s:
+        for op, q in pools:
+            t0 = time.perf_counter()
+            oracle.decode(op, 0, 0, q, wl.table, wl.seq)
+            spent += time.perf_counter() - t0
+            done_bytes += wl.kv_bytes_per_call
+            calls += 1
+            if spent >= budget_s:
+                break
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{calls} of {len(wl.order)} bank decode calls of one {wl.name} step "
-                      f"({wl.batch} requests, all heads), fp64, {spent:.1f} s"}
+            "sample": f"{calls} bank decode calls ({len(wl.snap)} distinct banks of the "
+                      f"{len(wl.order)} in one {wl.name} step, {wl.batch} requests, all heads), "
+                      f"fp64 oracle, {spent:.1f} s"}
 
 
 # --------------------------------------------------------------------------- main
@@ -209,6 +329,7 @@ def run_decode(args):
 
     wl = make_workload(args.workload, args.partition,
                        0 if args.no_cpu_baseline else args.cpu_banks)
+    wl.separate_write = args.separate_write
     nb = len(wl.order)
     for _ in range(args.warmup):
         wl.step()
@@ -228,18 +349,20 @@ def run_decode(args):
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # Per-launch timing of the decode call (partial + combine kernels), again
-    # over K steps, bracketing every decode call with events on the same stream.
-    evs = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in range(nb * args.steps)]
+    # The decode calls alone, back to back over K rounds of every bank, between
+    # two events on the stream the library launches on: the average duration
+    # of the dominant kernel (its combine kernel included when the split
+    # needs one; the fused store_kv included when the step fuses it).
     torch.cuda.synchronize()
-    for s in range(args.steps):
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(args.steps):
         for i in range(nb):
-            wl.call(i, evs[s * nb + i])
+            wl.call(i, decode_only=True)
+    d1.record(stream)
     torch.cuda.synchronize()
-    per_call_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    avg_call_s = float(per_call_ms.mean()) / 1e3
-
+    avg_call_s = d0.elapsed_time(d1) / 1e3 / (args.steps * nb)
     step_bytes = wl.kv_bytes_per_call * nb
     value = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = wl.kv_bytes_per_call / avg_call_s / 1e9
@@ -259,21 +382,22 @@ def run_decode(args):
         "config": dict(CONFIG_TEXT[wl.name], partition=wl.partition),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "tokens_planes_per_s": round(wl.batch * nb / (ms_per_step / 1e3), 1),
-        "decode_call_us": {"mean": round(float(per_call_ms.mean()) * 1e3, 2),
-                           "p10": round(float(np.percentile(per_call_ms, 10)) * 1e3, 2),
-                           "p90": round(float(np.percentile(per_call_ms, 90)) * 1e3, 2)},
+        "step": "paged_kv_write + paged_decode_attn" if wl.separate_write
+                else "paged_decode_append_attn (store_kv of the newest token fused)",
+        "decode_call_us": round(avg_call_s * 1e6, 2),
+        "split": wl.split,
         "kv_bytes_per_call": wl.kv_bytes_per_call,
         "unique_kv_bytes_per_call": wl.unique_bytes_per_call,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(wl.name),
-                     "kernel": "decode_partial_valu (split-K + in-kernel combine)"},
+                     "kernel": wl.kernel_name},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
-    return res
+    return res, wl
 
 
 def run_probe(kind: str):
@@ -308,6 +432,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ouro", choices=["ouro", "huginn", "longctx"])
     ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-supplementary", action="store_true",
+                    help="skip the 8 x 2048-token prefill shape")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="paged_kv_write + paged_decode_attn per bank instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--probe", choices=["copy", "read"], default=None,
@@ -330,7 +460,11 @@ def main():
         print(json.dumps(run_probe(args.probe)), flush=True)
         return
     log(f"device: {torch.cuda.get_device_name(0)}; workload {args.workload}")
-    res = run_decode(args)
+    res, wl = run_decode(args)
+    if not args.no_prefill:
+        del wl
+        torch.cuda.empty_cache()
+        res["prefill"] = run_prefill(supplementary=not args.no_supplementary)
     print(json.dumps(res), flush=True)
 
 

@@ -158,6 +158,33 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                       void *out, float *lse, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* Which split paged_decode_attn takes for these sizes: 0 = whole contexts
+ * (one workgroup per request and kv head), 1 = balanced split + combine,
+ * 2 = fixed partitions (+ combine when a context spans several). Host only;
+ * negative on invalid sizes. */
+int paged_decode_split_mode(const pkv_pool *pool, int32_t batch, int32_t num_q_heads,
+                            int32_t max_seq_len, int32_t partition);
+
+/* One decode step of a layer in one call: store_kv of each request's newest
+ * token followed by decode attention ([FFM] "So why is this hard...": a
+ * decode step appends exactly one slot per request). For each request r with
+ * n = seq_lens[r] > 0, k_new[r][h][:] and v_new[r][h][:] (DEVICE
+ * [batch][num_kv_heads][head_dim], pool dtype, 16-byte aligned) are written
+ * to position n - 1, i.e. page page_table[r][(n - 1) / 16], offset
+ * (n - 1) % 16, of bank bank_of[plane_id][layer_id], and then attended
+ * exactly as paged_decode_attn would after a paged_kv_write of the same rows:
+ * the results and the pool contents are bitwise identical to that pair of
+ * calls. The page holding position n - 1 must not be shared with another
+ * request of the same call (the newest token's page is private). All other
+ * arguments as for paged_decode_attn. */
+int paged_decode_append_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                             const void *k_new, const void *v_new, const void *q,
+                             int32_t num_q_heads, const int32_t *page_table,
+                             int32_t page_table_stride, const int32_t *seq_lens,
+                             int32_t batch, int32_t max_seq_len, float scale,
+                             int32_t partition, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* The split-K combine for fixed partitions on its own (the second kernel of
  * paged_decode_attn with partition > 0, usable on partials gathered from
  * elsewhere, e.g. other devices). For each row i = r *

@@ -50,7 +50,8 @@ class _Pool(ctypes.Structure):
 
 
 EXPORTS = ("pkv_bank_map", "pkv_pool_bytes", "paged_kv_write", "paged_decode_workspace_bytes",
-           "paged_decode_attn", "paged_decode_reduce", "paged_prefill_attn", "pkv_last_error")
+           "paged_decode_attn", "paged_decode_append_attn", "paged_decode_split_mode",
+           "paged_decode_reduce", "paged_prefill_attn", "pkv_last_error")
 
 
 def lib():
@@ -72,6 +73,11 @@ def lib():
         L.paged_decode_attn.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, i32, ctypes.c_float,
                                         i32, P, P, P, sz, P]
         L.paged_decode_attn.restype = ctypes.c_int
+        L.paged_decode_append_attn.argtypes = [P, i32, i32, P, P, P, i32, P, i32, P, i32, i32,
+                                               ctypes.c_float, i32, P, P, P, sz, P]
+        L.paged_decode_append_attn.restype = ctypes.c_int
+        L.paged_decode_split_mode.argtypes = [P, i32, i32, i32, i32]
+        L.paged_decode_split_mode.restype = ctypes.c_int
         L.paged_decode_reduce.argtypes = [i32, i32, i32, i32, P, i32, i32, P, P, P, P, P, P]
         L.paged_decode_reduce.restype = ctypes.c_int
         L.paged_prefill_attn.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, P, i32, i32, i32,
@@ -168,10 +174,22 @@ def workspace_bytes(pool: "Pool", batch: int, num_q_heads: int, max_seq_len: int
                                                   partition))
 
 
+SPLIT_MODES = {0: "whole", 1: "balanced", 2: "fixed"}
+
+
+def split_mode(pool: "Pool", batch: int, num_q_heads: int, max_seq_len: int,
+               partition: int = 0) -> str:
+    """The work split paged_decode_attn takes for these sizes."""
+    return SPLIT_MODES[_check(lib().paged_decode_split_mode(pool.ref, batch, num_q_heads,
+                                                           max_seq_len, partition))]
+
+
 def decode(pool: Pool, plane: int, layer: int, q, page_table, seq_lens, max_seq_len: int,
            scale: float | None = None, partition: int = 0, out=None, lse=None,
-           workspace=None, with_lse: bool = True, stream=None):
+           workspace=None, with_lse: bool = True, stream=None, k_new=None, v_new=None):
     """Decode attention. q [B, Hq, D]; page_table [B, stride] int32; seq_lens [B] int32.
+    With k_new, v_new [B, Hkv, D]: the decode step that first appends each
+    request's newest token at position seq_len - 1 (one kernel).
 
     Returns (out [B, Hq, D], lse [B, Hq] fp32 or None)."""
     torch = _torch()
@@ -186,6 +204,13 @@ def decode(pool: Pool, plane: int, layer: int, q, page_table, seq_lens, max_seq_
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    if k_new is not None:
+        _check(lib().paged_decode_append_attn(
+            pool.ref, plane, layer, _dptr(k_new), _dptr(v_new), _dptr(q), Hq,
+            _dptr(page_table), int(page_table.shape[1]), _dptr(seq_lens), B, max_seq_len,
+            float(scale), partition, _dptr(out), _dptr(lse), _dptr(workspace), ws_bytes,
+            _stream(stream)))
+        return out, lse
     _check(lib().paged_decode_attn(pool.ref, plane, layer, _dptr(q), Hq, _dptr(page_table),
                                    int(page_table.shape[1]), _dptr(seq_lens), B, max_seq_len,
                                    float(scale), partition, _dptr(out), _dptr(lse),

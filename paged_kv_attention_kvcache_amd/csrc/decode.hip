@@ -45,7 +45,9 @@ __global__ __launch_bounds__(kBlock) void decode_block(
     const int32_t *__restrict__ page_table, int32_t pt_stride,
     const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale, int32_t partition,
     int32_t max_parts, typename E::storage *__restrict__ out, float *__restrict__ lse,
-    float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc) {
+    float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc,
+    const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
+    uint4 *kb_w, uint4 *vb_w) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   __shared__ float2 lds_ml[kWaves * G];
   __shared__ float lds_acc[kWaves * G * D];
@@ -64,9 +66,15 @@ __global__ __launch_bounds__(kBlock) void decode_block(
   const int p_first = lo / kPage;
   const int n_pages = hi > lo ? (hi - 1) / kPage - p_first + 1 : 0;
   const int npw = n_pages > w ? (n_pages - w + kWaves - 1) / kWaves : 0;
+  const int32_t *pt_row = page_table + (size_t)r * pt_stride;
+  if (k_new && n > 0 && n - 1 >= lo && n - 1 < hi) {
+    const int pa = (n - 1) / kPage;  // page of the newest token
+    if ((pa - p_first) % kWaves == w)
+      f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
+                   n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
+  }
   if (npw > 0)
-    stream_pages(f, st, kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh,
-                 p_first + w, npw, kWaves, lo, hi);
+    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p_first + w, npw, kWaves, lo, hi);
   f.finish_wave(st);
   emit_to_lds(f, st, w, lds_ml, lds_acc);
   __syncthreads();
@@ -123,7 +131,9 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
                      static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
                      a.pt_stride, a.seq_lens, a.max_seq_len, a.scale * kLog2e, a.partition,
                      a.max_parts, static_cast<typename E::storage *>(a.out), a.lse, a.part_m,
-                     a.part_l, a.part_acc);
+                     a.part_l, a.part_acc, static_cast<const typename E::storage *>(a.k_new),
+                     static_cast<const typename E::storage *>(a.v_new),
+                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, D, a.seq_lens, a.max_seq_len,

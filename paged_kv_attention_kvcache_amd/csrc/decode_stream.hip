@@ -73,7 +73,9 @@ __global__ __launch_bounds__(kBlock) void decode_stream(
     const int32_t *__restrict__ page_table, int32_t pt_stride,
     const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
     typename E::storage *__restrict__ out, float *__restrict__ lse,
-    float2 *__restrict__ part_ml, float *__restrict__ part_acc) {
+    float2 *__restrict__ part_ml, float *__restrict__ part_acc,
+    const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
+    uint4 *kb_w, uint4 *vb_w) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   extern __shared__ int cum[];  // [batch + 1]
   row_prefix(seq_lens, batch, max_seq_len, hkv, cum);
@@ -103,8 +105,14 @@ __global__ __launch_bounds__(kBlock) void decode_stream(
     F f(q + row0 * D, qscale);
     typename F::State st;
     f.reset(st);
-    stream_pages(f, st, kb, vb, page_table + (size_t)r * pt_stride, num_pages, hkv, kvh, p, len,
-                 1, 0, n);
+    const int32_t *pt_row = page_table + (size_t)r * pt_stride;
+    if (k_new && n > 0) {
+      const int pa = (n - 1) / kPage;  // page of the newest token
+      if (pa >= p && pa < p + len)
+        f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
+                     n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
+    }
+    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p, len, 1, 0, n);
     f.finish_wave(st);
     if (p == 0 && len == pr) {  // the whole unit: finish here
       emit_final<F, E>(f, st, out, lse, row0);
@@ -282,7 +290,10 @@ static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t str
                      static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
                      a.pt_stride, a.seq_lens, a.batch, a.max_seq_len, a.scale * kLog2e,
                      static_cast<typename E::storage *>(a.out), a.lse,
-                     reinterpret_cast<float2 *>(a.part_m), a.part_acc);
+                     reinterpret_cast<float2 *>(a.part_m), a.part_acc,
+                     static_cast<const typename E::storage *>(a.k_new),
+                     static_cast<const typename E::storage *>(a.v_new),
+                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_stream_combine<E, G>), dim3(a.batch * a.bank.num_kv_heads),

@@ -46,6 +46,10 @@ struct MfmaFold {
   float qscale;
   int n, g4;
   uint32_t koff, voff;
+  // Appended token (decode step): page index in the request, offset in the
+  // page (-1: none), this lane's K chunks (as in Regs::k) and V chunk.
+  int app_page = -1, app_tok = -1;
+  uint4 app_k[4], app_v;
 
   __device__ __forceinline__ static bf16x8 as_bf16(const uint4 &x) {
     return __builtin_bit_cast(bf16x8, x);
@@ -62,6 +66,27 @@ struct MfmaFold {
     for (int c = 0; c < 4; ++c)
       qb[c] = n < G ? *reinterpret_cast<const uint4 *>(qrow + n * 128 + (4 * c + g4) * 8)
                     : make_uint4(0, 0, 0, 0);
+  }
+
+  // Makes this wave the writer of the request's newest token at position pos:
+  // its rows go to the tile of page id `page`, and the fold uses them for
+  // that position.
+  __device__ __forceinline__ void set_append(const uint16_t *__restrict__ k_row,
+                                             const uint16_t *__restrict__ v_row, int pos,
+                                             uint4 *__restrict__ kb, uint4 *__restrict__ vb,
+                                             int page, int hkv, int kvh) {
+    app_page = pos / kPage;
+    app_tok = pos % kPage;
+    const uint4 *kr = reinterpret_cast<const uint4 *>(k_row);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) app_k[c] = kr[4 * c + g4];
+    app_v = reinterpret_cast<const uint4 *>(v_row)[n];
+    const size_t row = ((size_t)page * hkv + kvh) * 256 + (size_t)app_tok * 16;
+    if (n == app_tok) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kb[row + 4 * c + g4] = app_k[c];
+    }
+    if (g4 == 0) vb[row + n] = app_v;
   }
 
   __device__ __forceinline__ void reset(State &st) const {
@@ -91,8 +116,21 @@ struct MfmaFold {
 
   // Folds pages piA and piB (piB = -1: absent) of the request; keys outside
   // [lo, hi) are masked.
-  __device__ __forceinline__ void fold(State &st, const Regs &r, int piA, int piB, int lo,
+  __device__ __forceinline__ void fold(State &st, Regs &r, int piA, int piB, int lo,
                                        int hi) const {
+    // The appended token replaces what the tile held.
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      if ((P == 0 ? piA : piB) == app_page) {
+        if (n == app_tok) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) r.k[P][c] = app_k[c];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * g4 + i == app_tok) r.v[P][i] = app_v;
+      }
+    }
     f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {

@@ -46,6 +46,10 @@ struct ValuFold {
   float qscale;
   int row, c;
   uint32_t lane_off;  // bytes into a tile
+  // Appended token (decode step): its page index in the request, its offset
+  // in that page (-1: none) and this lane's 16-byte chunk of its K and V rows.
+  int app_page = -1, app_tok = -1;
+  uint4 app_k, app_v;
 
   // qrow: the first of the G query rows (contiguous, head_dim each).
   __device__ __forceinline__ ValuFold(const typename E::storage *__restrict__ qrow, float qs)
@@ -57,6 +61,25 @@ struct ValuFold {
     const uint4 *qv = reinterpret_cast<const uint4 *>(qrow);
 #pragma unroll
     for (int g = 0; g < G; ++g) q[g].set(qv[g * LPT + c]);
+  }
+
+  // Makes this wave the writer of the request's newest token: position pos
+  // (page pos / 16) gets k_row / v_row (head_dim elements each) in the tile of
+  // page id `page`, and the fold uses these values for that position.
+  __device__ __forceinline__ void set_append(const typename E::storage *__restrict__ k_row,
+                                             const typename E::storage *__restrict__ v_row,
+                                             int pos, uint4 *__restrict__ kb,
+                                             uint4 *__restrict__ vb, int page, int hkv,
+                                             int kvh) {
+    app_page = pos / kPage;
+    app_tok = pos % kPage;
+    app_k = reinterpret_cast<const uint4 *>(k_row)[c];
+    app_v = reinterpret_cast<const uint4 *>(v_row)[c];
+    if (row == app_tok % RPW) {
+      const size_t at = ((size_t)page * hkv + kvh) * TL::kTileVec + (size_t)app_tok * LPT + c;
+      kb[at] = app_k;
+      vb[at] = app_v;
+    }
   }
 
   __device__ __forceinline__ void reset(State &st) const {
@@ -84,8 +107,16 @@ struct ValuFold {
   }
 
   // Folds page pi of the request (keys outside [lo, hi) masked).
-  __device__ __forceinline__ void fold(State &st, const Regs &r, int pi, int, int lo,
+  __device__ __forceinline__ void fold(State &st, Regs &r, int pi, int, int lo,
                                        int hi) const {
+    if (pi == app_page) {  // the appended token replaces what the tile held
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (row + i * RPW == app_tok) {
+          r.k[i] = app_k;
+          r.v[i] = app_v;
+        }
+    }
     const int pos0 = pi * kPage + row;  // token of load i: pos0 + i * RPW
     const bool full = (pi * kPage >= lo) && (pi * kPage + kPage <= hi);
     float s[G][NI];

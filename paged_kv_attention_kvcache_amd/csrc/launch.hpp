@@ -36,6 +36,10 @@ struct DecodeArgs {
   void *out;
   float *lse;
   float *part_m, *part_l, *part_acc;
+  // Decode step with append: each request's newest token (position
+  // seq_len - 1), [batch][num_kv_heads][head_dim], written and attended in
+  // the same kernel. NULL: the pool already holds it.
+  const void *k_new = nullptr, *v_new = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

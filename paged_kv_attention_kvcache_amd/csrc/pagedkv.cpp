@@ -191,11 +191,13 @@ size_t paged_decode_workspace_bytes(const pkv_pool *pool, int32_t batch, int32_t
   return 2 * align_up(rows * parts * sizeof(float)) + align_up(rows * parts * D * sizeof(float));
 }
 
-int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
-                      int32_t num_q_heads, const int32_t *page_table, int32_t page_table_stride,
-                      const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float scale,
-                      int32_t partition, void *out, float *lse, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+namespace {
+
+int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *k_new,
+                const void *v_new, const void *q, int32_t num_q_heads,
+                const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
+                int32_t batch, int32_t max_seq_len, float scale, int32_t partition, void *out,
+                float *lse, void *workspace, size_t workspace_bytes, void *stream) {
   pkv::Bank bank;
   int rc = resolve_bank(pool, plane_id, layer_id, &bank);
   if (rc) return rc;
@@ -235,6 +237,8 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, 
   a.max_parts = max_parts;
   a.out = out;
   a.lse = lse;
+  a.k_new = k_new;
+  a.v_new = v_new;
   char *ws = static_cast<char *>(workspace);
   if (stream_mode) {
     const int64_t nw = stream_wave_count(pool, batch, num_q_heads, max_seq_len);
@@ -242,14 +246,52 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, 
     a.part_m = reinterpret_cast<float *>(ws);
     a.part_acc = reinterpret_cast<float *>(ws + align_up(slots * 2 * sizeof(float)));
     return launched(pkv::launch_decode_stream(a, nw, static_cast<hipStream_t>(stream)),
-                    "paged_decode_attn");
+                    "decode");
   }
   const size_t rows = (size_t)batch * num_q_heads;
   const size_t ml = align_up(rows * max_parts * sizeof(float));
   a.part_m = reinterpret_cast<float *>(ws);
   a.part_l = reinterpret_cast<float *>(ws + ml);
   a.part_acc = reinterpret_cast<float *>(ws + 2 * ml);
-  return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), "paged_decode_attn");
+  return launched(pkv::launch_decode(a, static_cast<hipStream_t>(stream)), "decode");
+}
+
+}  // namespace
+
+int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
+                      int32_t num_q_heads, const int32_t *page_table, int32_t page_table_stride,
+                      const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float scale,
+                      int32_t partition, void *out, float *lse, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return decode_impl(pool, plane_id, layer_id, nullptr, nullptr, q, num_q_heads, page_table,
+                     page_table_stride, seq_lens, batch, max_seq_len, scale, partition, out, lse,
+                     workspace, workspace_bytes, stream);
+}
+
+int paged_decode_append_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                             const void *k_new, const void *v_new, const void *q,
+                             int32_t num_q_heads, const int32_t *page_table,
+                             int32_t page_table_stride, const int32_t *seq_lens, int32_t batch,
+                             int32_t max_seq_len, float scale, int32_t partition, void *out,
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!k_new || !v_new) return fail(PKV_EINVAL, "k_new / v_new is NULL");
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  return decode_impl(pool, plane_id, layer_id, k_new, v_new, q, num_q_heads, page_table,
+                     page_table_stride, seq_lens, batch, max_seq_len, scale, partition, out, lse,
+                     workspace, workspace_bytes, stream);
+}
+
+int paged_decode_split_mode(const pkv_pool *pool, int32_t batch, int32_t num_q_heads,
+                            int32_t max_seq_len, int32_t partition) {
+  if (!pool || pool->num_kv_heads <= 0 || batch <= 0 || num_q_heads <= 0 || partition < 0)
+    return fail(PKV_EINVAL, "bad sizes");
+  switch (decode_mode(batch, pool->num_kv_heads, max_seq_len, partition)) {
+    case Mode::kWhole: return 0;
+    case Mode::kStream: return 1;
+    case Mode::kFixed: return 2;
+  }
+  return 2;
 }
 
 int paged_decode_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads, int32_t head_dim,

@@ -44,7 +44,7 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
     auto load = [&](typename F::Regs &r, int s) {
       f.load(r, kb, vb, page(s * S), page(s * S + S - 1), hkv, kvh);
     };
-    auto fold = [&](const typename F::Regs &r, int s) {
+    auto fold = [&](typename F::Regs &r, int s) {
       f.fold(st, r, index(s * S), S > 1 ? index(s * S + 1) : -1, lo, hi);
     };
     typename F::Regs ra, rb;

@@ -146,6 +146,36 @@ def test_decode_parity(name, seed):
             check(f"{name}/s{seed}/q{q_scale}/p{partition}", case.layout.dtype, out, ro, rl, lse)
 
 
+APPEND_CASES = ["c1_tiny_f32", "c2_ouro", "c3_huginn", "c5_longctx", "bf16_d128_g4",
+                "bf16_d64_g4"]
+
+
+@pytest.mark.parametrize("partition", [0, 64])
+@pytest.mark.parametrize("name", APPEND_CASES)
+def test_decode_append_equals_write_then_attend(name, partition):
+    """paged_decode_append_attn == paged_kv_write + paged_decode_attn, bitwise,
+    outputs and pool bytes; and within tolerance of the oracle."""
+    import torch
+
+    kw = DECODE_CASES[name]
+    case = synth.make_decode_case(8, **kw)
+    dt = case.layout.dtype
+    bd = case.banks[(0, 0)]
+    out_a, lse_a, pool_a = gpu_decode_case(case, partition=partition)
+    pool_b = gpu_pool(case.layout)
+    write(pool_b, 0, 0, bd.fill_k, bd.fill_v, bd.fill_slots, dt)
+    out_b, lse_b = pkv.decode(pool_b, 0, 0, to_dev(bd.q, dt), i32_dev(case.page_table),
+                              i32_dev(case.seq_lens), int(case.seq_lens.max()),
+                              partition=partition, k_new=to_dev(bd.new_k, dt),
+                              v_new=to_dev(bd.new_v, dt))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(pool_a.k), bits(pool_b.k))
+    assert np.array_equal(bits(pool_a.v), bits(pool_b.v))
+    assert np.array_equal(bits(out_a), bits(out_b)) and np.array_equal(bits(lse_a), bits(lse_b))
+    ro, rl, _ = oracle_decode_case(case)
+    check(f"append/{name}/p{partition}", dt, out_b, ro, rl, lse_b)
+
+
 @pytest.mark.parametrize("partition", [0, 16, 32, 512])
 def test_decode_edge_lengths(partition):
     # seq_len 0 (empty row), 1, page and partition boundaries, a ragged tail
