@@ -75,5 +75,8 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// Matrix-core prefill (bf16, head_dim 128); launch_prefill picks it when it applies.
+bool prefill_mfma_supported(const PrefillArgs &a);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace pkv

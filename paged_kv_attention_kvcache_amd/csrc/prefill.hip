@@ -1,4 +1,5 @@
-// Chunked causal prefill over paged context for gfx950 (vector-ALU path).
+// Chunked causal prefill over paged context for gfx950, vector-ALU path
+// (fp32 data and head_dim 64; bf16 at head_dim 128 runs on matrix cores).
 //
 // An extend-prefill of a span ("Faster fuzzy minds", section "LOTUS"; a
 // prefix-cache hit prefills only the suffix, section "When scheduler does
@@ -81,6 +82,7 @@ static hipError_t prefill_by_group(const PrefillArgs &a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   if (a.total_q == 0) return hipSuccess;
+  if (prefill_mfma_supported(a)) return launch_prefill_mfma(a, stream);
   if (a.bank.dtype == 1)
     return a.bank.head_dim == 128 ? prefill_by_group<BF16, 128>(a, stream)
                                   : prefill_by_group<BF16, 64>(a, stream);
