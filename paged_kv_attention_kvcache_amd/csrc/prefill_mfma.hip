@@ -6,21 +6,36 @@
 // attend); packed query row j of request r sits at position seq_len - q_len
 // + j and sees keys 0..that position.
 //
-// Work: one workgroup per (tile of 128 query rows, q head, request); wave w
-// owns rows 32w .. 32w+31 of the tile as two blocks of 16 query columns. The
-// contraction runs on v_mfma_f32_16x16x32_bf16 in the transposed form
-//   S^T = K Q^T (A = 16 keys x 32 dims, B = 32 dims x 16 queries),
+// Work: one workgroup per (tile of 128 query rows, q head, request), launched
+// heaviest tiles (latest rows, most keys) first; wave w owns rows 32w..32w+31
+// of the tile as two blocks of 16 query columns. The contraction runs on
+// v_mfma_f32_16x16x32_bf16 in the transposed form
+//   S^T = K Q^T   (A = 16 keys x 32 dims from a row-major K tile),
 //   O^T += V^T P^T (A = 16 dims x 32 keys, B = 32 keys x 16 queries),
-// with the key index of P^T and V^T permuted so that P^T is each lane's own
-// scores (lane l: keys 4(l/16)+i of both pages of a step, query l%16).
-// Keys go by steps of two pages (32 keys): the workgroup copies the step's
-// K and V tiles (4 x 4 KiB) from HBM into LDS once, with the 16-byte chunk
-// index of each token row XOR-swizzled by the token so that the MFMA-layout
-// reads below are bank-conflict free, double-buffered (the next step's
-// global loads are in flight during the current step's math) with one
-// barrier per step. Both query blocks of a wave share each K and V read.
-// Steps past a wave's last query are skipped; only steps that cross the
-// diagonal are masked. Tiles are launched heaviest (latest rows) first.
+// where the key index of P^T and V^T is permuted so that P^T is each lane's
+// own scores (lane l: keys 4(l/16)+i of two pages, query l%16) and V^T comes
+// straight from a row-major V tile through ds_read_b64_tr_b16 (lane j of a
+// 16-lane group receives element j%4 of the 8-byte runs that lanes 4e + j/4
+// address, e = 0..3: four consecutive keys of one dim).
+//
+// Keys go in steps of four pages (64 keys). Each step's 4 K and 4 V tiles
+// (32 KiB) are copied from HBM straight into LDS with global_load_lds_dwordx4
+// (no register staging), into a ring of four stages: three steps are in
+// flight while one is folded. Each wave waits for its own copies with an
+// explicit vmcnt and one barrier per step publishes the stage (the compiler
+// does not track these copies, so the waits are written out). Within a
+// 256-byte token row the 16-byte chunk c of token t sits at c ^ rot(t)
+// (rot: 4-bit left rotation), which keeps both the K reads (16 tokens, one
+// chunk) and the transposing V reads (8 tokens, two chunks) free of bank
+// conflicts.
+//
+// Softmax: scores in base 2; the column max is a lane-swap reduction
+// (v_permlane32_swap, v_permlane16_swap); the output accumulators are
+// rescaled only when a column's max grows by more than 2^8 over the max in
+// use (the probabilities are then at most 256, exact in fp32 and bf16's
+// range), so most steps do no rescaling at all.
+#include <cfloat>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "span.hpp"
@@ -30,225 +45,333 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kTileRows = 128;   // query rows per workgroup
-constexpr int kBlocksPerWave = 2;  // 16-query column blocks per wave
-constexpr int kStepKeys = 32;    // keys per step (two pages)
-constexpr int kTileChunks = 256;  // 16-byte chunks in a (page, kv head) tile
-constexpr int kStage = 4 * kTileChunks;  // K page A, K page B, V page A, V page B
+constexpr int kTileRows = 128;                            // query rows per workgroup
+constexpr int kStepPages = 4;                             // pages per step
+constexpr int kStepKeys = kStepPages * kPage;             // 64
+constexpr int kRing = 4;                                  // LDS stages
+constexpr int kTileBytes = 4096;                          // one (page, kv head) tile
+constexpr int kStageBytes = 2 * kStepPages * kTileBytes;  // K and V tiles of a step
+constexpr int kMaxPages = 4096;                           // page ids held in LDS
+constexpr float kLazy = 8.f;                              // rescale threshold (log2 units)
 
 __device__ __forceinline__ bf16x8 as_bf16(const uint4 &x) { return __builtin_bit_cast(bf16x8, x); }
 
-// LDS slot of chunk c of token t in a tile (c ^ t spreads a column of the
-// tile over all 16 four-bank groups).
-__device__ __forceinline__ int swz(int t, int c) { return t * 16 + (c ^ t); }
+// 4-bit left rotation: the chunk swizzle of token t within a tile row.
+__device__ __forceinline__ int rot4(int t) { return ((t << 1) | (t >> 3)) & 15; }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_char *)p;
+}
+
+// 16 bytes per lane from global memory (base + voff) to LDS (m0 + 16 * lane).
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void *base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds));
+}
+
+// Waits until at most N of this wave's copies are outstanding (and its LDS
+// reads are done), then meets the other waves.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ bf16x4 read_tr(const lds_char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+}
+
+// max(a, b, c) as one v_max3_f32. fmaxf would first quiet possible
+// signalling NaNs of every operand (one more instruction each); the scores
+// here are finite or -inf.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// Max / sum over the four lanes of a query column (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float col_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = max3(__uint_as_float(a[0]), __uint_as_float(a[1]), -INFINITY);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max3(__uint_as_float(b[0]), __uint_as_float(b[1]), -INFINITY);
+}
+__device__ __forceinline__ float col_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 }  // namespace
 
 __global__ __launch_bounds__(kBlock) void prefill_mfma(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
-    const uint16_t *__restrict__ q, int32_t hq, const int32_t *__restrict__ cu_q_lens,
-    const int32_t *__restrict__ page_table, int32_t pt_stride,
-    const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale,
+    const uint16_t *__restrict__ q, int32_t hq, int32_t batch, int32_t tiles,
+    const int32_t *__restrict__ cu_q_lens, const int32_t *__restrict__ page_table,
+    int32_t pt_stride, const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale,
     uint16_t *__restrict__ out, float *__restrict__ lse) {
-  __shared__ uint4 stage[2][kStage];
+  __shared__ __attribute__((aligned(1024))) uint4 ring[kRing * kStageBytes / 16];
+  __shared__ int32_t pids[kMaxPages];
 
-  const int r = blockIdx.z, h = blockIdx.y;
-  const int G = hq / hkv, kvh = h / G;
+  // Heaviest tiles first; within a tile index, the q heads of one request are
+  // adjacent (the heads of a GQA group read the same K/V).
+  const int per_t = hq * batch;
+  const int id = (int)blockIdx.x;
+  const int t = tiles - 1 - id / per_t;
+  const int h = (id % per_t) % hq, r = (id % per_t) / hq;
+  const int kvh = h / (hq / hkv);
   const int q0 = cu_q_lens[r];
   const int n = min(max(seq_lens[r], 0), max_seq_len);
   const int q_len = min(max(cu_q_lens[r + 1] - q0, 0), n);
-  const int tiles = (q_len + kTileRows - 1) / kTileRows;
-  const int t = (int)gridDim.x - 1 - (int)blockIdx.x;  // heaviest tiles first
-  if (t >= tiles) return;
+  if (t * kTileRows >= q_len) return;
   const int p0 = n - q_len;  // position of query row 0
   const int row_lo = t * kTileRows, row_hi = min(row_lo + kTileRows, q_len);
   const int key_end = p0 + row_hi;  // keys [0, key_end) are visible to the tile
   const int steps = (key_end + kStepKeys - 1) / kStepKeys;
-  const int kpages = (key_end + kPage - 1) / kPage;
+  const int kpages = min((key_end + kPage - 1) / kPage, kMaxPages);
   const int32_t *pt_row = page_table + (size_t)r * pt_stride;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, g4 = lane >> 4;
-  const int wrow0 = row_lo + w * 32;  // first row of this wave
-  const int wave_rows = max(0, min(32, row_hi - wrow0));
-  const int wave_last_pos = p0 + wrow0 + wave_rows - 1;  // last query position of the wave
+
+  for (int i = tid; i < kpages; i += kBlock) pids[i] = min(max(pt_row[i], 0), num_pages - 1);
+  __syncthreads();
+
+  // Copies: wave w moves tiles 2w and 2w+1 of every stage (tiles 0-3 are the
+  // step's K pages, 4-7 its V pages), 1 KiB (four token rows) per
+  // instruction; lane l of copy qq lands in LDS slot 64 qq + l, i.e. token
+  // 4 qq + l/16, swizzled chunk l%16, and so reads chunk (l%16) ^ rot(token).
+  uint32_t goff[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int tt = 4 * qq + (lane >> 4);
+    goff[qq] = (uint32_t)(tt * 16 + ((lane & 15) ^ rot4(tt))) * 16u;
+  }
+  const uint32_t ring0 = lds_addr(ring);
+  auto issue = [&](int j) {
+    const uint32_t dst = ring0 + (uint32_t)(j % kRing) * kStageBytes;
+    int pid[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      pid[u] = pids[min(j * kStepPages + ((2 * w + u) & 3), kpages - 1)];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tile = 2 * w + u;
+      const uint4 *src = (tile < 4 ? kb : vb) +
+                         ((size_t)__builtin_amdgcn_readfirstlane(pid[u]) * hkv + kvh) * 256;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) dma16(dst + tile * kTileBytes + qq * 1024, goff[qq], src);
+    }
+  };
 
   // Q operands (B of S^T): block b, query row wrow0 + 16b + nl, chunk 4c + g4.
-  uint4 qb[kBlocksPerWave][4];
+  // A negative scale moves into Q's sign bits (exact), so the scale applied
+  // to scores is positive; a zero scale becomes the smallest normal float
+  // (scores of at most ~1e4 then give exp2 of exactly 1).
+  float qs = qscale;
+  uint32_t sgn = 0;
+  if (qs < 0.f) {
+    qs = -qs;
+    sgn = 0x80008000u;
+  }
+  if (!(qs > 0.f)) qs = FLT_MIN;
+  const int wrow0 = row_lo + w * 32;
+  uint4 qb[2][4];
 #pragma unroll
-  for (int b = 0; b < kBlocksPerWave; ++b) {
+  for (int b = 0; b < 2; ++b) {
     const int row = wrow0 + 16 * b + nl;
     const bool ok = row < row_hi;
-    const uint4 *qr = reinterpret_cast<const uint4 *>(q + ((size_t)(q0 + (ok ? row : 0)) * hq + h) * 128);
+    const uint4 *qr =
+        reinterpret_cast<const uint4 *>(q + ((size_t)(q0 + (ok ? row : 0)) * hq + h) * 128);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qb[b][c] = ok ? qr[4 * c + g4] : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < 4; ++c) {
+      const uint4 x = qr[4 * c + g4];
+      qb[b][c] = ok ? make_uint4(x.x ^ sgn, x.y ^ sgn, x.z ^ sgn, x.w ^ sgn)
+                    : make_uint4(0, 0, 0, 0);
+    }
   }
-  f32x4 acc[kBlocksPerWave][8];
-  float m[kBlocksPerWave], l[kBlocksPerWave];
+
+  // LDS read offsets within a tile. K: token nl, chunk 4c + g4. V (transposed
+  // read for dims 16 sl .. +15): token 4 g4 + nl/4, dims 16 sl + 4 (nl%4) .. +3.
+  const int gk = rot4(nl);
+  uint32_t koff[4];
 #pragma unroll
-  for (int b = 0; b < kBlocksPerWave; ++b) {
+  for (int c = 0; c < 4; ++c) koff[c] = (uint32_t)(nl * 16 + ((4 * c + g4) ^ gk)) * 16u;
+  const int tv = 4 * g4 + (nl >> 2);
+  const int gv = rot4(tv);
+  uint32_t voff[8];
+#pragma unroll
+  for (int sl = 0; sl < 8; ++sl)
+    voff[sl] = (uint32_t)(tv * 16 + ((2 * sl + ((nl >> 1) & 1)) ^ gv)) * 16u + (nl & 1) * 8u;
+
+  f32x4 acc[2][8];
+  float m[2], l[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[b] = -INFINITY;
     l[b] = 0.f;
   }
+  const int wave_rows = max(0, min(32, row_hi - wrow0));
+  const int wave_last = p0 + wrow0 + wave_rows - 1;  // last query position of the wave
 
-  // Global -> register copy of step s: thread tid moves chunk tid of each of
-  // the four tiles (token tid / 16, chunk tid % 16).
-  auto fetch = [&](int s, uint4 (&g)[4]) {
-    const int pa = min(2 * s, kpages - 1), pb = min(2 * s + 1, kpages - 1);
-    const int ida = min(max(pt_row[pa], 0), num_pages - 1);
-    const int idb = min(max(pt_row[pb], 0), num_pages - 1);
-    const size_t ta = ((size_t)ida * hkv + kvh) * kTileChunks + tid;
-    const size_t tb = ((size_t)idb * hkv + kvh) * kTileChunks + tid;
-    g[0] = load_stream(kb + ta);
-    g[1] = load_stream(kb + tb);
-    g[2] = load_stream(vb + ta);
-    g[3] = load_stream(vb + tb);
-  };
-  auto put = [&](int buf, const uint4 (&g)[4]) {
-    const int slot = swz(tid >> 4, tid & 15);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) stage[buf][p * kTileChunks + slot] = g[p];
-  };
+  for (int j = 0; j < kRing - 1; ++j)
+    if (j < steps) issue(j);
 
-  uint4 g[4];
-  if (steps > 0) {
-    fetch(0, g);
-    put(0, g);
-  }
-  __syncthreads();
+  const lds_char *ringb = (const lds_char *)ring;
   for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < steps;
-    if (more) fetch(s + 1, g);  // in flight during this step's math
+    const int ahead = min(kRing - 2, steps - 1 - s);  // copies of later stages in flight
+    if (ahead >= 2)
+      wait_barrier<16>();
+    else if (ahead == 1)
+      wait_barrier<8>();
+    else
+      wait_barrier<0>();
+    if (s + kRing - 1 < steps) issue(s + kRing - 1);
+
     const int k0 = s * kStepKeys;
-    if (wave_rows > 0 && k0 <= wave_last_pos) {
-      const uint4 *st = stage[buf];
-      // S^T for both pages; K rows of this lane: token nl, chunk 4c + g4.
-      uint4 kr[2][4];
+    const lds_char *st = ringb + (s % kRing) * kStageBytes;
+    const bool tail = k0 + kStepKeys > n;
+    if (tail) {
+      // Token rows at or beyond the context end may hold anything (NaN
+      // included) and meet probability 0 in the PV product: zero their V.
+      lds_u32x4 *vst = (lds_u32x4 *)(st + 4 * kTileBytes);
 #pragma unroll
-      for (int P = 0; P < 2; ++P)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kr[P][c] = st[P * kTileChunks + swz(nl, 4 * c + g4)];
-      // V rows of this lane: token 4 g4 + i of each page, dims chunk nl.
-      uint4 vr[8];
-#pragma unroll
-      for (int P = 0; P < 2; ++P)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vr[4 * P + i] = st[(2 + P) * kTileChunks + swz(4 * g4 + i, nl)];
-      // Keys of this lane: k0 + 16 P + 4 g4 + i. Beyond the context they may
-      // hold anything: zero their V rows.
-      const bool diag = k0 + kStepKeys - 1 > p0 + wrow0;  // some key after some row
-      if (k0 + kStepKeys > n) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k0 + 16 * (e >> 2) + 4 * g4 + (e & 3) >= n) vr[e] = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int chunk = tid + kBlock * i;  // V tile i, token tid / 16
+        if (k0 + 16 * i + (tid >> 4) >= n) vst[chunk] = u32x4{0u, 0u, 0u, 0u};
       }
-      // V^T operands (shared by both query blocks): dim slice j.
-      uint4 va[8];
-      auto word = [](const uint4 &x, int i) { return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w; };
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    if (wave_rows == 0 || k0 > wave_last) continue;  // nothing visible to this wave
+
+    // S^T for the four pages, both query blocks (K reads shared).
+    f32x4 S[2][4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t a[4];
+    for (int P = 0; P < 4; ++P) {
+      uint4 kr[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t x = word(vr[2 * kk], j >> 1), y = word(vr[2 * kk + 1], j >> 1);
-          a[kk] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        }
-        va[j] = make_uint4(a[0], a[1], a[2], a[3]);
-      }
+      for (int c = 0; c < 4; ++c)
+        kr[c] = __builtin_bit_cast(uint4, *(const lds_u32x4 *)(st + P * kTileBytes + koff[c]));
 #pragma unroll
-      for (int b = 0; b < kBlocksPerWave; ++b) {
-        const int qpos = p0 + wrow0 + 16 * b + nl;  // this lane's query position
-        if (p0 + wrow0 + 16 * b > wave_last_pos) continue;  // block past the tile
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < 2; ++b) {
+        S[b][P] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kr[0][c]), as_bf16(qb[b][c]), sa, 0, 0, 0);
-          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kr[1][c]), as_bf16(qb[b][c]), sb, 0, 0, 0);
-        }
-        float sv[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = sa[i] * qscale;
-          sv[4 + i] = sb[i] * qscale;
-        }
-        if (diag || k0 + kStepKeys > n) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kpos = k0 + 16 * (e >> 2) + 4 * g4 + (e & 3);
-            if (kpos > qpos || kpos >= n) sv[e] = -INFINITY;
-          }
-        }
-        float mx = sv[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m[b], mx);
-        const float ms = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(m[b] - ms);
-        float p[8], lsum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(sv[e] - ms);
-          lsum += p[e];
-        }
-        l[b] = l[b] * alpha + lsum;
-        m[b] = mn;
-        uint4 pw;
-        pw.x = pack_bf16x2(p[0], p[1]);
-        pw.y = pack_bf16x2(p[2], p[3]);
-        pw.z = pack_bf16x2(p[4], p[5]);
-        pw.w = pack_bf16x2(p[6], p[7]);
-        const bf16x8 pb = as_bf16(pw);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          acc[b][j] *= alpha;
-          acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(va[j]), pb, acc[b][j], 0, 0, 0);
-        }
+        for (int c = 0; c < 4; ++c)
+          S[b][P] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kr[c]), as_bf16(qb[b][c]),
+                                                            S[b][P], 0, 0, 0);
       }
     }
-    if (more) put(buf ^ 1, g);
-    __syncthreads();
+    // Keys after a query or beyond the context are masked (only on steps
+    // that cross the diagonal or the end of the context).
+    if (tail || k0 + kStepKeys - 1 > p0 + wrow0) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int qpos = p0 + wrow0 + 16 * b + nl;
+#pragma unroll
+        for (int P = 0; P < 4; ++P)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * P + 4 * g4 + i;
+            if (key > qpos || key >= n) S[b][P][i] = -INFINITY;
+          }
+      }
+    }
+
+    uint4 pb[2][2];  // P^T operands [block][half step]: keys 4 g4 + i of pages 2hs, 2hs+1
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float mx = max3(S[b][0][0], S[b][0][1], S[b][0][2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) mx = max3(mx, S[b][e >> 2][e & 3], S[b][(e + 1) >> 2][(e + 1) & 3]);
+      mx = max3(mx, S[b][3][3], S[b][3][3]);
+      const float mxs = col_max(mx) * qs;
+      if (__any(mxs > m[b] + kLazy)) {
+        const float mn = fmaxf(m[b], mxs);
+        const float alpha = fast_exp2(m[b] - ((mn == -INFINITY) ? 0.f : mn));
+        l[b] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[b][j] *= alpha;
+        m[b] = mn;
+      }
+      const float nms = (m[b] == -INFINITY) ? 0.f : -m[b];
+      float p[4][4], lsum = 0.f;
+#pragma unroll
+      for (int P = 0; P < 4; ++P)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[P][i] = fast_exp2(fmaf(S[b][P][i], qs, nms));
+          lsum += p[P][i];
+        }
+      l[b] += lsum;
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        pb[b][hs].x = pack_bf16x2(p[2 * hs][0], p[2 * hs][1]);
+        pb[b][hs].y = pack_bf16x2(p[2 * hs][2], p[2 * hs][3]);
+        pb[b][hs].z = pack_bf16x2(p[2 * hs + 1][0], p[2 * hs + 1][1]);
+        pb[b][hs].w = pack_bf16x2(p[2 * hs + 1][2], p[2 * hs + 1][3]);
+      }
+    }
+
+    // O^T += V^T P^T, 32 keys (pages 2hs, 2hs+1) at a time.
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const uint2 a = __builtin_bit_cast(uint2, read_tr(st + (4 + 2 * hs) * kTileBytes + voff[sl]));
+        const uint2 c = __builtin_bit_cast(uint2, read_tr(st + (5 + 2 * hs) * kTileBytes + voff[sl]));
+        const uint4 v = make_uint4(a.x, a.y, c.x, c.y);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[b][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(v), as_bf16(pb[b][hs]),
+                                                               acc[b][sl], 0, 0, 0);
+      }
+    }
   }
 
   // Sum each column's l over its four lane groups, then write O and lse.
+  // Lane (nl, g4) holds dims 16 sl + 4 g4 + i of query nl.
 #pragma unroll
-  for (int b = 0; b < kBlocksPerWave; ++b) {
-    float lt = l[b] + __shfl_xor(l[b], 16);
-    lt += __shfl_xor(lt, 32);
+  for (int b = 0; b < 2; ++b) {
+    const float lt = col_sum(l[b]);
     const int row = wrow0 + 16 * b + nl;
     if (row >= row_hi) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    float o[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[8 * i + j] = acc[b][j][i] * inv;
     const size_t rowh = (size_t)(q0 + row) * hq + h;
-    store_row<BF16>(out + rowh * 128 + 32 * g4, o, 32);
+    uint2 *orow = reinterpret_cast<uint2 *>(out + rowh * 128 + 4 * g4);
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+      orow[4 * sl] = make_uint2(pack_bf16x2(acc[b][sl][0] * inv, acc[b][sl][1] * inv),
+                                pack_bf16x2(acc[b][sl][2] * inv, acc[b][sl][3] * inv));
     if (lse && g4 == 0) lse[rowh] = lt > 0.f ? (m[b] + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
 bool prefill_mfma_supported(const PrefillArgs &a) {
-  return a.bank.dtype == 1 && a.bank.head_dim == 128;
+  return a.bank.dtype == 1 && a.bank.head_dim == 128 && a.max_seq_len <= kMaxPages * kPage;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
   const int tiles = (a.max_q_len + kTileRows - 1) / kTileRows;
   if (tiles == 0) return hipSuccess;
-  const dim3 grid(tiles, a.num_q_heads, a.batch);
-  hipLaunchKernelGGL(prefill_mfma, grid, dim3(kBlock), 0, stream,
+  const long long blocks = (long long)tiles * a.num_q_heads * a.batch;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_mfma, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads, static_cast<const uint16_t *>(a.q),
-                     a.num_q_heads, a.cu_q_lens, a.page_table, a.pt_stride, a.seq_lens,
-                     a.max_seq_len, a.scale * kLog2e, static_cast<uint16_t *>(a.out), a.lse);
+                     a.num_q_heads, a.batch, tiles, a.cu_q_lens, a.page_table, a.pt_stride,
+                     a.seq_lens, a.max_seq_len, a.scale * kLog2e, static_cast<uint16_t *>(a.out),
+                     a.lse);
   return hipGetLastError();
 }
 
