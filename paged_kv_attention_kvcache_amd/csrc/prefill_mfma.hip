@@ -20,8 +20,9 @@
 //
 // Keys go in steps of four pages (64 keys). Each step's 4 K and 4 V tiles
 // (32 KiB) are copied from HBM straight into LDS with global_load_lds_dwordx4
-// (no register staging), into a ring of four stages: three steps are in
-// flight while one is folded. Each wave waits for its own copies with an
+// (no register staging), into a ring of stages: with two stages (two
+// workgroups per CU) the next step is in flight while one is folded, with
+// four (one workgroup per CU, longer contexts) the next three are. Each wave waits for its own copies with an
 // explicit vmcnt and one barrier per step publishes the stage (the compiler
 // does not track these copies, so the waits are written out). Within a
 // 256-byte token row the 16-byte chunk c of token t sits at c ^ rot(t)
@@ -52,14 +53,9 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kTileRows = 128;                            // query rows per workgroup
-constexpr int kStepPages = 4;                             // pages per step
-constexpr int kStepKeys = kStepPages * kPage;             // 64
-constexpr int kRing = 4;                                  // LDS stages
-constexpr int kTileBytes = 4096;                          // one (page, kv head) tile
-constexpr int kStageBytes = 2 * kStepPages * kTileBytes;  // K and V tiles of a step
-constexpr int kMaxPages = 4096;                           // page ids held in LDS
-constexpr float kLazy = 8.f;                              // rescale threshold (log2 units)
+constexpr int kTileRows = 128;    // query rows per workgroup
+constexpr int kTileBytes = 4096;  // one (page, kv head) tile
+constexpr float kLazy = 8.f;      // rescale threshold (log2 units)
 
 __device__ __forceinline__ bf16x8 as_bf16(const uint4 &x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -80,6 +76,18 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, const void *b
 template <int N>
 __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// The same with N = PER * min(ahead, A) (a wait count must be an immediate).
+template <int PER, int A>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (A == 0) {
+    wait_barrier<0>();
+  } else {
+    if (ahead >= A)
+      wait_barrier<PER * A>();
+    else
+      wait_ahead<PER, A - 1>(ahead);
+  }
 }
 
 __device__ __forceinline__ bf16x4 read_tr(const lds_char *p) {
@@ -111,14 +119,20 @@ __device__ __forceinline__ float col_sum(float x) {
 
 }  // namespace
 
+// SP: pages per step; RING: LDS stages; MAXP: page ids held in LDS.
+template <int SP, int RING, int MAXP>
 __global__ __launch_bounds__(kBlock) void prefill_mfma(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
     const uint16_t *__restrict__ q, int32_t hq, int32_t batch, int32_t tiles,
     const int32_t *__restrict__ cu_q_lens, const int32_t *__restrict__ page_table,
     int32_t pt_stride, const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale,
     uint16_t *__restrict__ out, float *__restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) uint4 ring[kRing * kStageBytes / 16];
-  __shared__ int32_t pids[kMaxPages];
+  constexpr int kStepKeys = SP * kPage;
+  constexpr int kStageBytes = 2 * SP * kTileBytes;  // K and V tiles of a step
+  constexpr int kTPW = 2 * SP / kWaves;             // tiles each wave copies per step
+  static_assert(kTPW >= 1 && SP % 2 == 0, "a step is an even number of pages");
+  __shared__ __attribute__((aligned(1024))) uint4 ring[RING * kStageBytes / 16];
+  __shared__ int32_t pids[MAXP];
 
   // Heaviest tiles first; within a tile index, the q heads of one request are
   // adjacent (the heads of a GQA group read the same K/V).
@@ -135,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   const int row_lo = t * kTileRows, row_hi = min(row_lo + kTileRows, q_len);
   const int key_end = p0 + row_hi;  // keys [0, key_end) are visible to the tile
   const int steps = (key_end + kStepKeys - 1) / kStepKeys;
-  const int kpages = min((key_end + kPage - 1) / kPage, kMaxPages);
+  const int kpages = min((key_end + kPage - 1) / kPage, MAXP);
   const int32_t *pt_row = page_table + (size_t)r * pt_stride;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -145,9 +159,9 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   for (int i = tid; i < kpages; i += kBlock) pids[i] = min(max(pt_row[i], 0), num_pages - 1);
   __syncthreads();
 
-  // Copies: wave w moves tiles 2w and 2w+1 of every stage (tiles 0-3 are the
-  // step's K pages, 4-7 its V pages), 1 KiB (four token rows) per
-  // instruction; lane l of copy qq lands in LDS slot 64 qq + l, i.e. token
+  // Copies: wave w moves tiles kTPW w .. kTPW w + kTPW - 1 of every stage
+  // (tiles 0..SP-1 are the step's K pages, SP..2SP-1 its V pages), 1 KiB
+  // (four token rows) per instruction; lane l of copy qq lands in LDS slot 64 qq + l, i.e. token
   // 4 qq + l/16, swizzled chunk l%16, and so reads chunk (l%16) ^ rot(token).
   uint32_t goff[4];
 #pragma unroll
@@ -157,15 +171,15 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   }
   const uint32_t ring0 = lds_addr(ring);
   auto issue = [&](int j) {
-    const uint32_t dst = ring0 + (uint32_t)(j % kRing) * kStageBytes;
-    int pid[2];
+    const uint32_t dst = ring0 + (uint32_t)(j % RING) * kStageBytes;
+    int pid[kTPW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      pid[u] = pids[min(j * kStepPages + ((2 * w + u) & 3), kpages - 1)];
+    for (int u = 0; u < kTPW; ++u)
+      pid[u] = pids[min(j * SP + (kTPW * w + u) % SP, kpages - 1)];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tile = 2 * w + u;
-      const uint4 *src = (tile < 4 ? kb : vb) +
+    for (int u = 0; u < kTPW; ++u) {
+      const int tile = kTPW * w + u;
+      const uint4 *src = (tile < SP ? kb : vb) +
                          ((size_t)__builtin_amdgcn_readfirstlane(pid[u]) * hkv + kvh) * 256;
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) dma16(dst + tile * kTileBytes + qq * 1024, goff[qq], src);
@@ -225,29 +239,24 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   const int wave_last = p0 + wrow0 + wave_rows - 1;  // last query position of the wave
 
 #pragma unroll
-  for (int j = 0; j < kRing - 1; ++j)
+  for (int j = 0; j < RING - 1; ++j)
     if (j < steps) issue(j);
 
   const lds_char *ringb = (const lds_char *)ring;
   for (int s = 0; s < steps; ++s) {
-    const int ahead = min(kRing - 2, steps - 1 - s);  // copies of later stages in flight
-    if (ahead >= 2)
-      wait_barrier<16>();
-    else if (ahead == 1)
-      wait_barrier<8>();
-    else
-      wait_barrier<0>();
-    if (s + kRing - 1 < steps) issue(s + kRing - 1);
+    // stages issued after this one, each kTPW * 4 copies per wave
+    wait_ahead<kTPW * 4, RING - 2>(min(RING - 2, steps - 1 - s));
+    if (s + RING - 1 < steps) issue(s + RING - 1);
 
     const int k0 = s * kStepKeys;
-    const lds_char *st = ringb + (s % kRing) * kStageBytes;
+    const lds_char *st = ringb + (s % RING) * kStageBytes;
     const bool tail = k0 + kStepKeys > n;
     if (tail) {
       // Token rows at or beyond the context end may hold anything (NaN
       // included) and meet probability 0 in the PV product: zero their V.
-      lds_u32x4 *vst = (lds_u32x4 *)(st + 4 * kTileBytes);
+      lds_u32x4 *vst = (lds_u32x4 *)(st + SP * kTileBytes);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < SP; ++i) {
         const int chunk = tid + kBlock * i;  // V tile i, token tid / 16
         if (k0 + 16 * i + (tid >> 4) >= n) vst[chunk] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -256,9 +265,9 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
     if (wave_rows == 0 || k0 > wave_last) continue;  // nothing visible to this wave
 
     // S^T for the four pages, both query blocks (K reads shared).
-    f32x4 S[2][4];
+    f32x4 S[2][SP];
 #pragma unroll
-    for (int P = 0; P < 4; ++P) {
+    for (int P = 0; P < SP; ++P) {
       uint4 kr[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
       for (int b = 0; b < 2; ++b) {
         const int qpos = p0 + wrow0 + 16 * b + nl;
 #pragma unroll
-        for (int P = 0; P < 4; ++P)
+        for (int P = 0; P < SP; ++P)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = k0 + 16 * P + 4 * g4 + i;
@@ -288,13 +297,12 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
       }
     }
 
-    uint4 pb[2][2];  // P^T operands [block][half step]: keys 4 g4 + i of pages 2hs, 2hs+1
+    uint4 pb[2][SP / 2];  // P^T operands [block][half step]: keys 4 g4 + i of pages 2hs, 2hs+1
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      float mx = max3(S[b][0][0], S[b][0][1], S[b][0][2]);
+      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 3; e < 15; e += 2) mx = max3(mx, S[b][e >> 2][e & 3], S[b][(e + 1) >> 2][(e + 1) & 3]);
-      mx = max3(mx, S[b][3][3], S[b][3][3]);
+      for (int e = 0; e < 4 * SP; e += 2) mx = max3(mx, S[b][e >> 2][e & 3], S[b][e >> 2][(e & 3) + 1]);
       const float mxs = col_max(mx) * qs;
       if (__any(mxs > m[b] + kLazy)) {
         const float mn = fmaxf(m[b], mxs);
@@ -305,9 +313,9 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
         m[b] = mn;
       }
       const float nms = (m[b] == -INFINITY) ? 0.f : -m[b];
-      float p[4][4], lsum = 0.f;
+      float p[SP][4], lsum = 0.f;
 #pragma unroll
-      for (int P = 0; P < 4; ++P)
+      for (int P = 0; P < SP; ++P)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           p[P][i] = fast_exp2(fmaf(S[b][P][i], qs, nms));
@@ -315,7 +323,7 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
         }
       l[b] += lsum;
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
+      for (int hs = 0; hs < SP / 2; ++hs) {
         pb[b][hs].x = pack_bf16x2(p[2 * hs][0], p[2 * hs][1]);
         pb[b][hs].y = pack_bf16x2(p[2 * hs][2], p[2 * hs][3]);
         pb[b][hs].z = pack_bf16x2(p[2 * hs + 1][0], p[2 * hs + 1][1]);
@@ -325,11 +333,11 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
 
     // O^T += V^T P^T, 32 keys (pages 2hs, 2hs+1) at a time.
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
+    for (int hs = 0; hs < SP / 2; ++hs) {
 #pragma unroll
       for (int sl = 0; sl < 8; ++sl) {
-        const uint2 a = __builtin_bit_cast(uint2, read_tr(st + (4 + 2 * hs) * kTileBytes + voff[sl]));
-        const uint2 c = __builtin_bit_cast(uint2, read_tr(st + (5 + 2 * hs) * kTileBytes + voff[sl]));
+        const uint2 a = __builtin_bit_cast(uint2, read_tr(st + (SP + 2 * hs) * kTileBytes + voff[sl]));
+        const uint2 c = __builtin_bit_cast(uint2, read_tr(st + (SP + 2 * hs + 1) * kTileBytes + voff[sl]));
         const uint4 v = make_uint4(a.x, a.y, c.x, c.y);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -357,8 +365,14 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   }
 }
 
+namespace {
+// One workgroup per CU: four 64-key stages (128 KiB) and page ids for 64k
+// tokens. Two per CU: two 64-key stages and page ids for 32k tokens.
+constexpr int kWideMaxPages = 4096, kNarrowMaxPages = 2048;
+}  // namespace
+
 bool prefill_mfma_supported(const PrefillArgs &a) {
-  return a.bank.dtype == 1 && a.bank.head_dim == 128 && a.max_seq_len <= kMaxPages * kPage;
+  return a.bank.dtype == 1 && a.bank.head_dim == 128 && a.max_seq_len <= kWideMaxPages * kPage;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
@@ -366,13 +380,20 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   const long long blocks = (long long)tiles * a.num_q_heads * a.batch;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_mfma, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
-                     static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
-                     a.bank.num_pages, a.bank.num_kv_heads, static_cast<const uint16_t *>(a.q),
-                     a.num_q_heads, a.batch, tiles, a.cu_q_lens, a.page_table, a.pt_stride,
-                     a.seq_lens, a.max_seq_len, a.scale * kLog2e, static_cast<uint16_t *>(a.out),
-                     a.lse);
-  return hipGetLastError();
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
+                       static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
+                       a.bank.num_pages, a.bank.num_kv_heads, static_cast<const uint16_t *>(a.q),
+                       a.num_q_heads, a.batch, tiles, a.cu_q_lens, a.page_table, a.pt_stride,
+                       a.seq_lens, a.max_seq_len, a.scale * kLog2e,
+                       static_cast<uint16_t *>(a.out), a.lse);
+    return hipGetLastError();
+  };
+  // Two workgroups per CU (72 KiB of LDS each) hide one another's copy
+  // waits and softmax; the four-stage single-workgroup kernel covers longer
+  // contexts.
+  if (a.max_seq_len <= kNarrowMaxPages * kPage) return go(prefill_mfma<4, 2, kNarrowMaxPages>);
+  return go(prefill_mfma<4, 4, kWideMaxPages>);
 }
 
 }  // namespace pkv

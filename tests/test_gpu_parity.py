@@ -282,6 +282,21 @@ def test_prefill_ragged(dtype, hq, hkv, D):
     _prefill_compare(f"ragged/{dtype}/{hq}x{hkv}x{D}", case, chunks, gp, op)
 
 
+@pytest.mark.parametrize("lens,start", [([36000, 1000], [35800, 900]),
+                                        ([70000], [69900])])
+def test_prefill_long_context(lens, start):
+    # suffixes over long cached prefixes: contexts past 32k tokens take the
+    # four-stage matrix-core kernel, past 64k tokens the vector-ALU kernel
+    say(f"prefill long context {lens}")
+    case = synth.make_prefill_case(6, "bf16", lens, 4, 2, 128)
+    gp, op = gpu_pool(case.layout), oracle_pool(case.layout)
+    k, v, s = synth.prefix_writes(case, start)
+    write(gp, 0, 0, k, v, s, "bf16")
+    oracle.kv_write(op, 0, 0, k, v, s)
+    _prefill_compare(f"long/{lens}", case, synth.chunk_schedule(case, 1 << 20, start=start),
+                     gp, op)
+
+
 # ------------------------------------------------------------------ bitwise invariants
 
 def test_decode_bitwise_invariants():
