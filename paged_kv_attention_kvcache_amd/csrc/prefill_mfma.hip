@@ -36,6 +36,7 @@
 // use (the probabilities are then at most 256, exact in fp32 and bf16's
 // range), so most steps do no rescaling at all.
 #include <cfloat>
+#include <utility>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -117,6 +118,16 @@ __device__ __forceinline__ float col_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 }  // namespace
 
 // SP: pages per step; RING: LDS stages; MAXP: page ids held in LDS.
@@ -170,8 +181,9 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
     goff[qq] = (uint32_t)(tt * 16 + ((lane & 15) ^ rot4(tt))) * 16u;
   }
   const uint32_t ring0 = lds_addr(ring);
-  auto issue = [&](int j) {
-    const uint32_t dst = ring0 + (uint32_t)(j % RING) * kStageBytes;
+  // Step j into ring slot `slot` (= j % RING, a compile-time constant).
+  auto issue = [&](int j, auto slot) {
+    const uint32_t dst = ring0 + (uint32_t)decltype(slot)::value * kStageBytes;
     int pid[kTPW];
 #pragma unroll
     for (int u = 0; u < kTPW; ++u)
@@ -226,6 +238,8 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   for (int sl = 0; sl < 8; ++sl)
     voff[sl] = (uint32_t)(tv * 16 + ((2 * sl + ((nl >> 1) & 1)) ^ gv)) * 16u + (nl & 1) * 8u;
 
+  // acc[b][sl]: O^T tiles; l[b]: this lane's part of the softmax denominator
+  // (its keys), summed in fp32 before the probabilities are rounded to bf16.
   f32x4 acc[2][8];
   float m[2], l[2];
 #pragma unroll
@@ -238,18 +252,22 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   const int wave_rows = max(0, min(32, row_hi - wrow0));
   const int wave_last = p0 + wrow0 + wave_rows - 1;  // last query position of the wave
 
-#pragma unroll
-  for (int j = 0; j < RING - 1; ++j)
-    if (j < steps) issue(j);
+  static_for<RING - 1>([&](auto j) {
+    if (decltype(j)::value < steps) issue(decltype(j)::value, j);
+  });
 
   const lds_char *ringb = (const lds_char *)ring;
-  for (int s = 0; s < steps; ++s) {
+  // One step; the stage index is a compile-time constant (the loop below is
+  // unrolled by RING), so every LDS address is a per-lane base plus an
+  // immediate offset.
+  auto step = [&](int s, auto stage) {
     // stages issued after this one, each kTPW * 4 copies per wave
     wait_ahead<kTPW * 4, RING - 2>(min(RING - 2, steps - 1 - s));
-    if (s + RING - 1 < steps) issue(s + RING - 1);
+    if (s + RING - 1 < steps)
+      issue(s + RING - 1, std::integral_constant<int, (decltype(stage)::value + RING - 1) % RING>{});
 
     const int k0 = s * kStepKeys;
-    const lds_char *st = ringb + (s % RING) * kStageBytes;
+    const lds_char *st = ringb + decltype(stage)::value * kStageBytes;
     const bool tail = k0 + kStepKeys > n;
     if (tail) {
       // Token rows at or beyond the context end may hold anything (NaN
@@ -262,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
       }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (wave_rows == 0 || k0 > wave_last) continue;  // nothing visible to this wave
+    if (wave_rows == 0 || k0 > wave_last) return;  // nothing visible to this wave
 
     // S^T for the four pages, both query blocks (K reads shared).
     f32x4 S[2][SP];
@@ -286,14 +304,13 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
     if (tail || k0 + kStepKeys - 1 > p0 + wrow0) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int qpos = p0 + wrow0 + 16 * b + nl;
+        // key k0 + 4 g4 + (16 P + i) is visible iff 16 P + i <= lim
+        const int lim = min(p0 + wrow0 + 16 * b + nl, n - 1) - k0 - 4 * g4;
 #pragma unroll
         for (int P = 0; P < SP; ++P)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 16 * P + 4 * g4 + i;
-            if (key > qpos || key >= n) S[b][P][i] = -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i)
+            if (16 * P + i > lim) S[b][P][i] = -INFINITY;
       }
     }
 
@@ -345,7 +362,11 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
                                                                acc[b][sl], 0, 0, 0);
       }
     }
-  }
+  };
+  for (int s0 = 0; s0 < steps; s0 += RING)
+    static_for<RING>([&](auto i) {
+      if (s0 + decltype(i)::value < steps) step(s0 + decltype(i)::value, i);
+    });
 
   // Sum each column's l over its four lane groups, then write O and lse.
   // Lane (nl, g4) holds dims 16 sl + 4 g4 + i of query nl.
