@@ -282,22 +282,28 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
     }
     if (wave_rows == 0 || k0 > wave_last) return;  // nothing visible to this wave
 
-    // S^T for the four pages, both query blocks (K reads shared).
+    // S^T for the step's pages, both query blocks (K reads shared), two pages
+    // at a time with the dim chunk outermost: consecutive MFMAs update four
+    // different accumulators, so none waits on the one before.
     f32x4 S[2][SP];
 #pragma unroll
-    for (int P = 0; P < SP; ++P) {
-      uint4 kr[4];
+    for (int P2 = 0; P2 < SP; P2 += 2) {
+      uint4 kr[2][4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        kr[c] = __builtin_bit_cast(uint4, *(const lds_u32x4 *)(st + P * kTileBytes + koff[c]));
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        S[b][P] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          S[b][P] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kr[c]), as_bf16(qb[b][c]),
-                                                            S[b][P], 0, 0, 0);
-      }
+          kr[pp][c] = __builtin_bit_cast(
+              uint4, *(const lds_u32x4 *)(st + (P2 + pp) * kTileBytes + koff[c]));
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            S[b][P2 + pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16(kr[pp][c]), as_bf16(qb[b][c]),
+                c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[b][P2 + pp], 0, 0, 0);
     }
     // Keys after a query or beyond the context are masked (only on steps
     // that cross the diagonal or the end of the context).
