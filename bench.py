@@ -436,6 +436,8 @@ def main():
                     help="skip the chunked-prefill measurement")
     ap.add_argument("--no-supplementary", action="store_true",
                     help="skip the 8 x 2048-token prefill shape")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the chunked-prefill measurement (one JSON line of its cases)")
     ap.add_argument("--separate-write", action="store_true",
                     help="paged_kv_write + paged_decode_attn per bank instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -460,6 +462,10 @@ def main():
         print(json.dumps(run_probe(args.probe)), flush=True)
         return
     log(f"device: {torch.cuda.get_device_name(0)}; workload {args.workload}")
+    if args.prefill_only:
+        print(json.dumps({"prefill": run_prefill(supplementary=not args.no_supplementary)}),
+              flush=True)
+        return
     res, wl = run_decode(args)
     if not args.no_prefill:
         del wl

@@ -3,6 +3,9 @@
     python -m paged_kv_attention_kvcache_amd.rocprof_summary stats DIR
         per-kernel calls / average / min / max duration from a
         `rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run` run;
+    python -m paged_kv_attention_kvcache_amd.rocprof_summary shapes DIR
+        the same per launch shape (kernel, grid size) from the kernel trace of
+        such a run, for kernels launched on inputs of several sizes;
     python -m paged_kv_attention_kvcache_amd.rocprof_summary pmc DIR
         per-kernel averages of every counter of a `--pmc` run;
     python -m paged_kv_attention_kvcache_amd.rocprof_summary traffic \\
@@ -71,6 +74,21 @@ def kernel_stats(d: str) -> list[dict]:
     return out
 
 
+def shape_stats(d: str) -> list[dict]:
+    """Calls / average / min / max duration per (kernel, grid size)."""
+    rows = csv.DictReader(open(_one(os.path.join(d, "*kernel_trace.csv"))))
+    acc = collections.defaultdict(list)
+    for r in rows:
+        grid = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        acc[(short_name(r["Kernel_Name"]), grid)].append(dur)
+    out = []
+    for (name, grid), ds in sorted(acc.items()):
+        out.append({"name": name, "grid": grid, "calls": len(ds), "avg_us": sum(ds) / len(ds),
+                    "min_us": min(ds), "max_us": max(ds)})
+    return out
+
+
 def pmc_averages(d: str) -> dict:
     """{kernel short name: {counter: mean over dispatches}}."""
     rows = csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv"))))
@@ -112,6 +130,8 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("--all", action="store_true", help="include kernels of other libraries")
+    sh = sub.add_parser("shapes")
+    sh.add_argument("dir")
     p = sub.add_parser("pmc")
     p.add_argument("dir")
     t = sub.add_parser("traffic")
@@ -126,6 +146,14 @@ def main(argv=None):
             if args.all or "pkv::" in r["name"]:
                 print(f"{r['name']:110s} {r['calls']:6d} {r['avg_us']:10.2f} {r['min_us']:10.2f} "
                       f"{r['max_us']:10.2f} {r['pct']:6.2f}")
+    elif args.cmd == "shapes":
+        print(f"{'kernel':60s} {'grid (threads)':>22s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} "
+              f"{'max_us':>10s}")
+        for r in shape_stats(args.dir):
+            if "pkv::" in r["name"]:
+                g = "x".join(str(v) for v in r["grid"])
+                print(f"{r['name'][:60]:60s} {g:>22s} {r['calls']:6d} {r['avg_us']:10.2f} "
+                      f"{r['min_us']:10.2f} {r['max_us']:10.2f}")
     elif args.cmd == "pmc":
         for k, cs in pmc_averages(args.dir).items():
             print(k)
