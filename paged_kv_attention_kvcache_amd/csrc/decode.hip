@@ -16,6 +16,16 @@
 
 namespace pkv {
 
+// Waves per decode workgroup. A workgroup streams one (request, kv head)
+// context and a wave's page loads in flight are bounded by its registers, so
+// a context's streaming rate grows with its waves: with 8 the longest
+// contexts (which set the call's duration) finish sooner. Such workgroups
+// fill a CU one at a time, so a call of many contexts runs in rounds; small
+// batches are then launched longest context first (request_of_rank) and
+// the short contexts fill in behind.
+constexpr int kDecodeWaves = 8;
+constexpr int kLptMaxBatch = 64;
+
 // Combines partitions 0 .. np-1 of row `rowh` (in order) for output dim d.
 __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
                                             const float *__restrict__ part_l,
@@ -36,10 +46,25 @@ __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
   }
 }
 
-// One workgroup per (partition j, kv head, request): the 4 waves take pages
-// w, w+4, ... of the partition, their states meet in LDS.
-template <typename E, class F>
-__global__ __launch_bounds__(kBlock) void decode_block(
+// The request of rank q when requests are ordered longest context first (ties
+// by index); batch <= 64, one request per lane. Every lane returns it.
+__device__ __forceinline__ int request_of_rank(const int32_t *__restrict__ seq_lens, int batch,
+                                               int max_seq_len, int q) {
+  const int lane = threadIdx.x & 63;
+  const int mine = lane < batch ? min(max(seq_lens[lane], 0), max_seq_len) : -1;
+  int rank = 0;
+  for (int j = 0; j < batch; ++j) {
+    const int o = __builtin_amdgcn_readlane(mine, j);
+    rank += (o > mine) || (o == mine && j < lane);
+  }
+  const unsigned long long hit = __ballot(lane < batch && rank == q);
+  return hit ? __ffsll(hit) - 1 : 0;
+}
+
+// One workgroup per (partition j, kv head, request): its W waves take pages
+// w, w+W, ... of the partition, their states meet in LDS.
+template <typename E, class F, int W>
+__global__ __launch_bounds__(64 * W) void decode_block(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
     const typename E::storage *__restrict__ q, int32_t hq,
     const int32_t *__restrict__ page_table, int32_t pt_stride,
@@ -47,12 +72,23 @@ __global__ __launch_bounds__(kBlock) void decode_block(
     int32_t max_parts, typename E::storage *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc,
     const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
-    uint4 *kb_w, uint4 *vb_w) {
+    uint4 *kb_w, uint4 *vb_w, int32_t batch, int32_t lpt) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
-  __shared__ float2 lds_ml[kWaves * G];
-  __shared__ float lds_acc[kWaves * G * D];
+  constexpr int kThreads = 64 * W;
+  __shared__ float2 lds_ml[W * G];
+  __shared__ float lds_acc[W * G * D];
 
-  const int j = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
+  const int j = blockIdx.x;
+  int kvh = blockIdx.y, r = blockIdx.z;
+  if (lpt) {
+    // One partition per request (gridDim.x == 1), launched in (request, kv
+    // head) order: the i-th workgroup takes the i-th (request, kv head) of the
+    // longest-first order, so when workgroups run in more than one round the
+    // longest contexts start first and the short ones fill the gaps.
+    const int i = blockIdx.z * gridDim.y + blockIdx.y;
+    kvh = i % hkv;
+    r = request_of_rank(seq_lens, batch, max_seq_len, i / hkv);
+  }
   const int n = min(max(seq_lens[r], 0), max_seq_len);
   const int np = min((n + partition - 1) / partition, max_parts);
   const int lo = j * partition;
@@ -65,34 +101,34 @@ __global__ __launch_bounds__(kBlock) void decode_block(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int p_first = lo / kPage;
   const int n_pages = hi > lo ? (hi - 1) / kPage - p_first + 1 : 0;
-  const int npw = n_pages > w ? (n_pages - w + kWaves - 1) / kWaves : 0;
+  const int npw = n_pages > w ? (n_pages - w + W - 1) / W : 0;
   const int32_t *pt_row = page_table + (size_t)r * pt_stride;
   if (k_new && n > 0 && n - 1 >= lo && n - 1 < hi) {
     const int pa = (n - 1) / kPage;  // page of the newest token
-    if ((pa - p_first) % kWaves == w)
+    if ((pa - p_first) % W == w)
       f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
                    n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
   }
   if (npw > 0)
-    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p_first + w, npw, kWaves, lo, hi);
+    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p_first + w, npw, W, lo, hi);
   f.finish_wave(st);
   emit_to_lds(f, st, w, lds_ml, lds_acc);
   __syncthreads();
 
   const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
   if (np <= 1) {  // the whole context in one partition: finish here
-    for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
       const int g = idx / D, d = idx % D;
       float M, L, A;
-      combine_waves<G, D>(lds_ml, lds_acc, g, d, M, L, A);
+      combine_waves<G, D, W>(lds_ml, lds_acc, g, d, M, L, A);
       finish<E>(out, lse, row0 + g, D, d, M, L, A);
     }
     return;
   }
-  for (int idx = threadIdx.x; idx < G * D; idx += kBlock) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int g = idx / D, d = idx % D;
     float M, L, A;
-    combine_waves<G, D>(lds_ml, lds_acc, g, d, M, L, A);
+    combine_waves<G, D, W>(lds_ml, lds_acc, g, d, M, L, A);
     const size_t pj = (row0 + g) * max_parts + j;
     part_acc[pj * D + d] = A;
     if (d == 0) {
@@ -125,7 +161,8 @@ template <typename E, int D, int G>
 static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
   using F = typename FoldFor<E, D, G>::type;
   const dim3 grid(a.max_parts, a.bank.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((decode_block<E, F>), grid, dim3(kBlock), 0, stream,
+  constexpr int W = kDecodeWaves;
+  hipLaunchKernelGGL((decode_block<E, F, W>), grid, dim3(64 * W), 0, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads,
                      static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
@@ -133,7 +170,8 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
                      a.max_parts, static_cast<typename E::storage *>(a.out), a.lse, a.part_m,
                      a.part_l, a.part_acc, static_cast<const typename E::storage *>(a.k_new),
                      static_cast<const typename E::storage *>(a.v_new),
-                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
+                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v), a.batch,
+                     (a.max_parts == 1 && a.batch <= kLptMaxBatch) ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, D, a.seq_lens, a.max_seq_len,

@@ -11,4 +11,5 @@ template <typename E, int D, int G> struct FoldFor { using type = ValuFold<E, D,
 template <> struct FoldFor<BF16, 128, 4> { using type = MfmaFold<4>; };
 template <> struct FoldFor<BF16, 128, 8> { using type = MfmaFold<8>; };
 
+
 }  // namespace pkv

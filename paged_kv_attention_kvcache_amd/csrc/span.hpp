@@ -6,8 +6,8 @@
 // folds them into its online-softmax state (F::fold). stream_pages() drives
 // any fold over a list of pages of one (request, kv head): page ids are
 // fetched one per lane, 64 at a time, ahead of the loop, and the loop is
-// software-pipelined two steps deep (the next step's K/V loads are in flight
-// while the current step is folded), so no load waits on a page-table read or
+// software-pipelined F::kDepth steps deep (the next steps' K/V loads are in
+// flight while the current step is folded), so no load waits on a page-table read or
 // on the previous step's math. After F::finish_wave(), F::emit() hands the
 // wave's state to a callback as (head g, first dim d0, count, m, l, acc[count])
 // slices, which the kernels route to LDS, to the output, or to split-K
@@ -47,23 +47,46 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
     auto fold = [&](typename F::Regs &r, int s) {
       f.fold(st, r, index(s * S), S > 1 ? index(s * S + 1) : -1, lo, hi);
     };
-    typename F::Regs ra, rb;
-    load(ra, 0);
-    int s = 0;
-    // Steady state: steps s+1 and s+2 both exist, so the prefetches are
-    // unconditional and each fold waits only for its own step's loads.
-    for (; s + 2 < steps; s += 2) {
-      load(rb, s + 1);
+    if constexpr (F::kDepth >= 3) {
+      // Three steps in flight: the steady state (all prefetches exist) runs
+      // unconditionally; at most four steps remain for the tail.
+      typename F::Regs ra, rb, rc;
+      load(ra, 0);
+      if (steps > 1) load(rb, 1);
+      int s = 0;
+      for (; s + 4 < steps; s += 3) {
+        load(rc, s + 2);
+        fold(ra, s);
+        load(ra, s + 3);
+        fold(rb, s + 1);
+        load(rb, s + 4);
+        fold(rc, s + 2);
+      }
+      if (s + 2 < steps) load(rc, s + 2);
       fold(ra, s);
-      load(ra, s + 2);
-      fold(rb, s + 1);
-    }
-    if (s + 1 < steps) {
-      load(rb, s + 1);
-      fold(ra, s);
-      fold(rb, s + 1);
+      if (s + 3 < steps) load(ra, s + 3);
+      if (s + 1 < steps) fold(rb, s + 1);
+      if (s + 2 < steps) fold(rc, s + 2);
+      if (s + 3 < steps) fold(ra, s + 3);
     } else {
-      fold(ra, s);
+      typename F::Regs ra, rb;
+      load(ra, 0);
+      int s = 0;
+      // Steady state: steps s+1 and s+2 both exist, so the prefetches are
+      // unconditional and each fold waits only for its own step's loads.
+      for (; s + 2 < steps; s += 2) {
+        load(rb, s + 1);
+        fold(ra, s);
+        load(ra, s + 2);
+        fold(rb, s + 1);
+      }
+      if (s + 1 < steps) {
+        load(rb, s + 1);
+        fold(ra, s);
+        fold(rb, s + 1);
+      } else {
+        fold(ra, s);
+      }
     }
   }
 }
@@ -79,18 +102,18 @@ __device__ __forceinline__ void emit_to_lds(F &f, const typename F::State &st, i
   });
 }
 
-// Combine the kWaves wave states of head g, dim d (in wave order).
-template <int G, int D>
+// Combine the W wave states of head g, dim d (in wave order).
+template <int G, int D, int W = kWaves>
 __device__ __forceinline__ void combine_waves(const float2 *lds_ml, const float *lds_acc,
                                               int g, int d, float &M, float &L, float &A) {
   M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds_ml[w * G + g].x);
+  for (int w = 0; w < W; ++w) M = fmaxf(M, lds_ml[w * G + g].x);
   const float ms = (M == -INFINITY) ? 0.f : M;
   L = 0.f;
   A = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     const float f = fast_exp2(lds_ml[w * G + g].x - ms);
     L = fmaf(lds_ml[w * G + g].y, f, L);
     A = fmaf(lds_acc[(w * G + g) * D + d], f, A);
