@@ -22,8 +22,12 @@ namespace pkv {
 // contexts (which set the call's duration) finish sooner. Such workgroups
 // fill a CU one at a time, so a call of many contexts runs in rounds; small
 // batches are then launched longest context first (request_of_rank) and
-// the short contexts fill in behind.
-constexpr int kDecodeWaves = 8;
+// the short contexts fill in behind. Folds of larger groups need more than
+// the 256 registers a wave of an 8-wave workgroup may hold: they use 4.
+template <class F>
+constexpr int decode_waves() {
+  return F::kGroup <= 2 ? 8 : 4;
+}
 constexpr int kLptMaxBatch = 64;
 
 // Combines partitions 0 .. np-1 of row `rowh` (in order) for output dim d.
@@ -161,7 +165,7 @@ template <typename E, int D, int G>
 static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
   using F = typename FoldFor<E, D, G>::type;
   const dim3 grid(a.max_parts, a.bank.num_kv_heads, a.batch);
-  constexpr int W = kDecodeWaves;
+  constexpr int W = decode_waves<F>();
   hipLaunchKernelGGL((decode_block<E, F, W>), grid, dim3(64 * W), 0, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads,

@@ -117,26 +117,39 @@ struct MfmaFold {
 
   // Folds pages piA and piB (piB = -1: absent) of the request; keys outside
   // [lo, hi) are masked.
-  __device__ __forceinline__ void fold(State &st, Regs &r, int piA, int piB, int lo,
+  __device__ __forceinline__ void fold(State &st, const Regs &r, int piA, int piB, int lo,
                                        int hi) const {
-    // The appended token replaces what the tile held.
+    // The page registers are only read (the loop that streams them keeps
+    // them in place); on the appended token's page a local copy carries its
+    // row.
+    if (piA == app_page || piB == app_page) {
+      Regs x = r;
 #pragma unroll
-    for (int P = 0; P < 2; ++P) {
-      if ((P == 0 ? piA : piB) == app_page) {
+      for (int P = 0; P < 2; ++P) {
+        if ((P == 0 ? piA : piB) != app_page) continue;
         if (n == app_tok) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) r.k[P][c] = app_k[c];
+          for (int c = 0; c < 4; ++c) x.k[P][c] = app_k[c];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * g4 + i == app_tok) r.v[P][i] = app_v;
+          if (4 * g4 + i == app_tok) x.v[P][i] = app_v;
       }
+      fold_regs(st, x, piA, piB, lo, hi);
+    } else {
+      fold_regs(st, r, piA, piB, lo, hi);
     }
+  }
+
+  __device__ __forceinline__ void fold_regs(State &st, const Regs &r, int piA, int piB, int lo,
+                                            int hi) const {
+    auto kk = [&](int P, int c) { return r.k[P][c]; };
+    auto vv = [&](int P, int i) { return r.v[P][i]; };
     f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(r.k[0][c]), as_bf16(qb[c]), sA, 0, 0, 0);
-      sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(r.k[1][c]), as_bf16(qb[c]), sB, 0, 0, 0);
+      sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kk(0, c)), as_bf16(qb[c]), sA, 0, 0, 0);
+      sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kk(1, c)), as_bf16(qb[c]), sB, 0, 0, 0);
     }
     const bool full = piA >= 0 && piB >= 0 && piA * kPage >= lo && piA * kPage + kPage <= hi &&
                       piB * kPage >= lo && piB * kPage + kPage <= hi;
@@ -176,8 +189,7 @@ struct MfmaFold {
     pw.w = pack_bf16x2(p[6], p[7]);
     const bf16x8 pb = as_bf16(pw);
 
-    uint4 vr[8] = {r.v[0][0], r.v[0][1], r.v[0][2], r.v[0][3],
-                   r.v[1][0], r.v[1][1], r.v[1][2], r.v[1][3]};
+    uint4 vr[8] = {vv(0, 0), vv(0, 1), vv(0, 2), vv(0, 3), vv(1, 0), vv(1, 1), vv(1, 2), vv(1, 3)};
     if (!full) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)

@@ -107,24 +107,38 @@ struct ValuFold {
     for (int i = 0; i < NI; ++i) r.v[i] = load_stream(vt + lane_off + i * RPW * LPT * 16u);
   }
 
-  // Folds page pi of the request (keys outside [lo, hi) masked).
-  __device__ __forceinline__ void fold(State &st, Regs &r, int pi, int, int lo,
+  // Folds page pi of the request (keys outside [lo, hi) masked). The page
+  // registers are only read (the loop that streams them keeps them in
+  // place); on the appended token's page a local copy carries its row.
+  __device__ __forceinline__ void fold(State &st, const Regs &r, int pi, int, int lo,
                                        int hi) const {
-    if (pi == app_page) {  // the appended token replaces what the tile held
+    if (pi == app_page) {
+      Regs x = r;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         if (row + i * RPW == app_tok) {
-          r.k[i] = app_k;
-          r.v[i] = app_v;
+          x.k[i] = app_k;
+          x.v[i] = app_v;
         }
+      fold_regs(st, x, pi, lo, hi);
+    } else {
+      fold_regs(st, r, pi, lo, hi);
     }
+  }
+
+  __device__ __forceinline__ void fold_regs(State &st, const Regs &r, int pi, int lo,
+                                            int hi) const {
+    auto kk = [&](int i) { return r.k[i]; };
+    auto vv = [&](int i) { return r.v[i]; };
     const int pos0 = pi * kPage + row;  // token of load i: pos0 + i * RPW
     const bool full = (pi * kPage >= lo) && (pi * kPage + kPage <= hi);
     float s[G][NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int i = 0; i < NI; ++i) {
+      const uint4 k = kk(i);
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g][i] = q[g].dot(r.k[i]);
+      for (int g = 0; g < G; ++g) s[g][i] = q[g].dot(k);
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -158,7 +172,7 @@ struct ValuFold {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[N];
-      Vec<E>::widen(r.v[i], vf);
+      Vec<E>::widen(vv(i), vf);
       if (!valid[i]) {
 #pragma unroll
         for (int e = 0; e < N; ++e) vf[e] = 0.f;

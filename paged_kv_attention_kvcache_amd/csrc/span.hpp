@@ -44,8 +44,13 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
     auto load = [&](typename F::Regs &r, int s) {
       f.load(r, kb, vb, page(s * S), page(s * S + S - 1), hkv, kvh);
     };
+    // A fold ends with a compiler-only barrier: the next load into the same
+    // registers must not be hoisted above it (that needs a second register
+    // set, and the copy between the two sets at the loop's back edge waits
+    // for every load in flight).
     auto fold = [&](typename F::Regs &r, int s) {
       f.fold(st, r, index(s * S), S > 1 ? index(s * S + 1) : -1, lo, hi);
+      asm volatile("" ::: "memory");
     };
     if constexpr (F::kDepth >= 3) {
       // Three steps in flight: the steady state (all prefetches exist) runs
