@@ -32,7 +32,7 @@ struct ValuFold {
   using TL = Tile<E, D>;
   static constexpr int N = TL::kVecN, LPT = TL::kLPT, RPW = TL::kRPW, NI = TL::kNI;
   static constexpr int kPagesPerStep = 1;
-  static constexpr int kDepth = 2;  // steps in flight per wave (3 costs occupancy)
+  static constexpr int kDepth = 2;  // steps in flight per wave (3 measured slower)
   static constexpr int kGroup = G;
   static constexpr int kHeadDim = D;
 
