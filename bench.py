@@ -112,7 +112,7 @@ class DecodeWorkload:
         g = hq // hkv
         fold = f"MfmaFold<{g}>" if g in (4, 8) and D == 128 else f"ValuFold<BF16, {D}, {g}>"
         self.kernel_name = {
-            "whole": f"decode_block<BF16, {fold}> (one launch per call)",
+            "whole": f"decode_whole<BF16, {fold}> (one launch per call)",
             "balanced": f"decode_stream<BF16, {fold}> + decode_stream_combine",
             "fixed": f"decode_block<BF16, {fold}> + decode_reduce"}[self.split]
         # algorithmic bytes: each request reads its whole context (K and V)
@@ -145,6 +145,13 @@ class DecodeWorkload:
     def step(self):
         for i in range(len(self.order)):
             self.call(i)
+
+    def step_graph(self):
+        """The same step (fused calls) captured once as one submission."""
+        pkv, nb = self.pkv, len(self.order)
+        return pkv.StepGraph(self.pool, self.order, self.q, self.table_d, self.seq_d,
+                             self.max_seq, [self.out] * nb, [self.lse] * nb, workspace=self.ws,
+                             k_new=self.nk, v_new=self.nv, partition=self.partition)
 
 
 def make_workload(name, partition, snapshot_banks=0):
@@ -364,6 +371,22 @@ def run_decode(args):
     torch.cuda.synchronize()
     avg_call_s = d0.elapsed_time(d1) / 1e3 / (args.steps * nb)
     step_bytes = wl.kv_bytes_per_call * nb
+
+    # The same step as one submission (paged_decode_step captured once, then
+    # replayed): K replays between two events.
+    graph = wl.step_graph()
+    for _ in range(max(args.warmup, 1)):
+        graph.launch(stream)
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.launch(stream)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / args.steps
+    graph.close()
     value = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = wl.kv_bytes_per_call / avg_call_s / 1e9
     res = {
@@ -382,6 +405,10 @@ def run_decode(args):
         "config": dict(CONFIG_TEXT[wl.name], partition=wl.partition),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "tokens_planes_per_s": round(wl.batch * nb / (ms_per_step / 1e3), 1),
+        "single_submission": {"ms_per_step": round(graph_ms, 4),
+                              "kv_GBps": round(step_bytes / (graph_ms / 1e3) / 1e9, 2),
+                              "tokens_planes_per_s": round(wl.batch * nb / (graph_ms / 1e3), 1),
+                              "how": "paged_decode_step_capture + graph launch per step"},
         "step": "paged_kv_write + paged_decode_attn" if wl.separate_write
                 else "paged_decode_append_attn (store_kv of the newest token fused)",
         "decode_call_us": round(avg_call_s * 1e6, 2),

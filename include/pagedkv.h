@@ -185,6 +185,54 @@ int paged_decode_append_attn(const pkv_pool *pool, int32_t plane_id, int32_t lay
                              int32_t partition, void *out, float *lse,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* One decode step of a looped model: the decode calls of every (plane,
+ * layer) the step visits, in the given order, enqueued by one host call
+ * ([FFM] "Recurrent depth": loop iteration t of layer l is one attention
+ * call on bank t*L + l, and the loop runs inside the model's forward; [PR152]
+ * "Notes" #148 submits a fixed-depth decode loop as one unit). Call i is
+ * paged_decode_append_attn on (plane_ids[i], layer_ids[i]) with k_new[i],
+ * v_new[i], q[i], out[i], lse[i] -- or paged_decode_attn when k_new and
+ * v_new are NULL (the arrays themselves, not their entries). plane_ids,
+ * layer_ids and the pointer arrays are HOST arrays of num_calls entries
+ * (lse may be NULL: no lse for any call); every other argument is shared by
+ * all calls and means what it means for paged_decode_attn. Every call is
+ * validated before the first is enqueued. The calls run one after another
+ * on `stream` and share the workspace. */
+int paged_decode_step(const pkv_pool *pool, int32_t num_calls, const int32_t *plane_ids,
+                      const int32_t *layer_ids, const void *const *k_new,
+                      const void *const *v_new, const void *const *q, int32_t num_q_heads,
+                      const int32_t *page_table, int32_t page_table_stride,
+                      const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float scale,
+                      int32_t partition, void *const *out, float *const *lse, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* A decode step recorded once and replayed as one submission ([FFM] "When
+ * scheduler does the work": a decode step has a fixed shape, so it is
+ * captured once as a graph and replayed; [PR152] "Notes" #148: the decode
+ * loop of a fixed-depth model as one submission). paged_decode_step_capture
+ * records paged_decode_step with these arguments into a HIP graph (stream
+ * capture on capture_stream, which must not be the null stream; nothing
+ * runs during capture) and returns it in *graph. A launch replays the whole
+ * step on `stream`, reading the device buffers' contents at replay time:
+ * q, k_new, v_new, page_table and seq_lens may change between replays
+ * (seq_lens within the captured max_seq_len), pointers and host sizes may
+ * not. The graph holds HIP runtime objects (host memory, and whatever the
+ * runtime allocates to instantiate it) until paged_decode_step_graph_destroy;
+ * the device buffers stay the caller's. Replays that share a workspace must
+ * not overlap. */
+typedef struct pkv_step_graph pkv_step_graph;
+int paged_decode_step_capture(const pkv_pool *pool, int32_t num_calls, const int32_t *plane_ids,
+                              const int32_t *layer_ids, const void *const *k_new,
+                              const void *const *v_new, const void *const *q,
+                              int32_t num_q_heads, const int32_t *page_table,
+                              int32_t page_table_stride, const int32_t *seq_lens, int32_t batch,
+                              int32_t max_seq_len, float scale, int32_t partition,
+                              void *const *out, float *const *lse, void *workspace,
+                              size_t workspace_bytes, void *capture_stream,
+                              pkv_step_graph **graph);
+int paged_decode_step_graph_launch(pkv_step_graph *graph, void *stream);
+void paged_decode_step_graph_destroy(pkv_step_graph *graph);
+
 /* The split-K combine for fixed partitions on its own (the second kernel of
  * paged_decode_attn with partition > 0, usable on partials gathered from
  * elsewhere, e.g. other devices). For each row i = r *
@@ -222,6 +270,25 @@ int paged_prefill_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                        const int32_t *seq_lens, int32_t batch,
                        int32_t max_q_len, int32_t max_seq_len, float scale,
                        void *out, float *lse, void *stream);
+
+/* One extend pass over a span in one call ([FFM] "LOTUS": a pass over the
+ * latent block writes the block's K/V to the slots it was handed -- the same
+ * slots on every pass, so each pass overwrites the last in place -- and is
+ * one parallel extend-prefill over all block positions). Exactly
+ * paged_kv_write(k, v, slot_mapping, total_q tokens) followed by
+ * paged_prefill_attn with the other arguments, on `stream`, with results
+ * and pool bytes bitwise identical to that pair of calls:
+ *   k, v:          DEVICE [total_q][num_kv_heads][head_dim], pool dtype,
+ *                  16-byte aligned; row i is the K/V of packed query row i
+ *   slot_mapping:  DEVICE int32 [total_q]; row i's slot, normally the slot
+ *                  of its own position n - q_len + j (negative: not written)
+ * Every argument is validated before anything is enqueued. */
+int paged_extend_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *k,
+                      const void *v, const int32_t *slot_mapping, const void *q,
+                      int32_t num_q_heads, const int32_t *cu_q_lens, int32_t total_q,
+                      const int32_t *page_table, int32_t page_table_stride,
+                      const int32_t *seq_lens, int32_t batch, int32_t max_q_len,
+                      int32_t max_seq_len, float scale, void *out, float *lse, void *stream);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *pkv_last_error(void);

@@ -51,7 +51,9 @@ class _Pool(ctypes.Structure):
 
 EXPORTS = ("pkv_bank_map", "pkv_pool_bytes", "paged_kv_write", "paged_decode_workspace_bytes",
            "paged_decode_attn", "paged_decode_append_attn", "paged_decode_split_mode",
-           "paged_decode_reduce", "paged_prefill_attn", "pkv_last_error")
+           "paged_decode_step", "paged_decode_step_capture", "paged_decode_step_graph_launch",
+           "paged_decode_step_graph_destroy", "paged_decode_reduce", "paged_prefill_attn",
+           "paged_extend_attn", "pkv_last_error")
 
 
 def lib():
@@ -78,11 +80,24 @@ def lib():
         L.paged_decode_append_attn.restype = ctypes.c_int
         L.paged_decode_split_mode.argtypes = [P, i32, i32, i32, i32]
         L.paged_decode_split_mode.restype = ctypes.c_int
+        step = [P, i32, P, P, P, P, P, i32, P, i32, P, i32, i32, ctypes.c_float, i32, P, P, P,
+                sz, P]
+        L.paged_decode_step.argtypes = step
+        L.paged_decode_step.restype = ctypes.c_int
+        L.paged_decode_step_capture.argtypes = step + [ctypes.POINTER(P)]
+        L.paged_decode_step_capture.restype = ctypes.c_int
+        L.paged_decode_step_graph_launch.argtypes = [P, P]
+        L.paged_decode_step_graph_launch.restype = ctypes.c_int
+        L.paged_decode_step_graph_destroy.argtypes = [P]
+        L.paged_decode_step_graph_destroy.restype = None
         L.paged_decode_reduce.argtypes = [i32, i32, i32, i32, P, i32, i32, P, P, P, P, P, P]
         L.paged_decode_reduce.restype = ctypes.c_int
         L.paged_prefill_attn.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, P, i32, i32, i32,
                                          ctypes.c_float, P, P, P]
         L.paged_prefill_attn.restype = ctypes.c_int
+        L.paged_extend_attn.argtypes = [P, i32, i32, P, P, P, P, i32, P, i32, P, i32, P, i32,
+                                        i32, i32, ctypes.c_float, P, P, P]
+        L.paged_extend_attn.restype = ctypes.c_int
         L.pkv_last_error.argtypes = []
         L.pkv_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -218,6 +233,94 @@ def decode(pool: Pool, plane: int, layer: int, q, page_table, seq_lens, max_seq_
     return out, lse
 
 
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _step_args(pool: Pool, calls, q, page_table, seq_lens, max_seq_len, scale, partition, out,
+               lse, workspace, k_new, v_new):
+    """Marshals a decode step: calls [(plane, layer)], per-call tensors q[i],
+    out[i], lse[i], k_new[i], v_new[i] (sequences or stacked tensors)."""
+    n = len(calls)
+    B, Hq, D = q[0].shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    planes = np.ascontiguousarray([c[0] for c in calls], dtype=np.int32)
+    layers = np.ascontiguousarray([c[1] for c in calls], dtype=np.int32)
+    keep = [planes, layers]
+    arrs = {}
+    for name, ts in (("q", q), ("out", out), ("lse", lse), ("k_new", k_new), ("v_new", v_new)):
+        if ts is None:
+            arrs[name] = None
+            continue
+        assert len(ts) == n, name
+        a = _ptr_array([ts[i] for i in range(n)])
+        keep.append(a)
+        arrs[name] = a
+    need = workspace_bytes(pool, B, Hq, max_seq_len, partition)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = [pool.ref, n, planes.ctypes.data, layers.ctypes.data, arrs["k_new"], arrs["v_new"],
+            arrs["q"], Hq, _dptr(page_table), int(page_table.shape[1]), _dptr(seq_lens), B,
+            max_seq_len, float(scale), partition, arrs["out"], arrs["lse"], _dptr(workspace),
+            ws_bytes]
+    return args, keep, need
+
+
+def decode_step(pool: Pool, calls, q, page_table, seq_lens, max_seq_len: int, out, lse=None,
+                workspace=None, k_new=None, v_new=None, scale: float | None = None,
+                partition: int = 0, stream=None) -> None:
+    """One decode step over several (plane, layer) banks in one C call
+    (paged_decode_step). q[i], out[i] [B, Hq, D]; lse[i] [B, Hq] or lse None;
+    k_new[i], v_new[i] [B, Hkv, D] or both None (no append)."""
+    if workspace is None:
+        torch = _torch()
+        B, Hq, _ = q[0].shape
+        workspace = torch.empty(max(workspace_bytes(pool, B, Hq, max_seq_len, partition), 1),
+                                dtype=torch.uint8, device=q[0].device)
+    args, keep, _ = _step_args(pool, calls, q, page_table, seq_lens, max_seq_len, scale,
+                               partition, out, lse, workspace, k_new, v_new)
+    _check(lib().paged_decode_step(*args, _stream(stream)))
+
+
+class StepGraph:
+    """A decode step captured once (paged_decode_step_capture) and replayed as
+    one submission. The tensors passed here are the step's fixed buffers:
+    replays read their contents at replay time."""
+
+    def __init__(self, pool: Pool, calls, q, page_table, seq_lens, max_seq_len: int, out,
+                 lse=None, workspace=None, k_new=None, v_new=None, scale: float | None = None,
+                 partition: int = 0):
+        torch = _torch()
+        if workspace is None:
+            B, Hq, _ = q[0].shape
+            workspace = torch.empty(max(workspace_bytes(pool, B, Hq, max_seq_len, partition), 1),
+                                    dtype=torch.uint8, device=q[0].device)
+        # keep every buffer the graph points at alive with the graph
+        self._bufs = (pool, q, page_table, seq_lens, out, lse, workspace, k_new, v_new)
+        args, self._keep, _ = _step_args(pool, calls, q, page_table, seq_lens, max_seq_len, scale,
+                                         partition, out, lse, workspace, k_new, v_new)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        torch.cuda.current_stream().synchronize()
+        handle = ctypes.c_void_p()
+        _check(lib().paged_decode_step_capture(*args, side.cuda_stream, ctypes.byref(handle)))
+        self._h = handle
+
+    def launch(self, stream=None) -> None:
+        _check(lib().paged_decode_step_graph_launch(self._h, _stream(stream)))
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            lib().paged_decode_step_graph_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def decode_reduce(dtype, seq_lens, partition: int, part_m, part_l, part_acc, out=None,
                   lse=None, stream=None):
     """Split-K combine. part_m/part_l [B, Hq, max_parts] fp32 (base-2 units),
@@ -254,3 +357,60 @@ def prefill(pool: Pool, plane: int, layer: int, q, cu_q_lens, page_table, seq_le
                                     _dptr(seq_lens), B, max_q_len, max_seq_len, float(scale),
                                     _dptr(out), _dptr(lse), _stream(stream)))
     return out, lse
+
+
+def extend(pool: Pool, plane: int, layer: int, k, v, slot_mapping, q, cu_q_lens, page_table,
+           seq_lens, max_q_len: int, max_seq_len: int, scale: float | None = None, out=None,
+           lse=None, with_lse: bool = True, stream=None):
+    """One extend pass (paged_extend_attn): store_kv of the span's k, v
+    [total_q, Hkv, D] to slot_mapping [total_q], then causal prefill of q
+    [total_q, Hq, D] over the context, in one call."""
+    torch = _torch()
+    total_q, Hq, D = q.shape
+    B = int(seq_lens.shape[0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    _check(lib().paged_extend_attn(pool.ref, plane, layer, _dptr(k), _dptr(v),
+                                   _dptr(slot_mapping), _dptr(q), Hq, _dptr(cu_q_lens), total_q,
+                                   _dptr(page_table), int(page_table.shape[1]), _dptr(seq_lens),
+                                   B, max_q_len, max_seq_len, float(scale), _dptr(out),
+                                   _dptr(lse), _stream(stream)))
+    return out, lse
+
+
+class LotusBlock:
+    """The in-place latent loop of one batch of requests on one bank: each
+    request's block of positions [start_r, start_r + block) is handed the
+    same slots on every pass, so pass k overwrites pass k-1's K/V and attends
+    the prefix plus its own block ("Faster fuzzy minds", section "LOTUS").
+    The slots are computed once, from the page table, when the loop starts.
+
+    pass_(k, v, q) runs one pass: k, v [B * block, Hkv, D] and q
+    [B * block, Hq, D], request-major."""
+
+    def __init__(self, pool: Pool, plane: int, layer: int, page_table, starts, block: int,
+                 page_size: int = 16):
+        torch = _torch()
+        starts = np.asarray(starts, np.int64)
+        table = page_table.cpu().numpy() if hasattr(page_table, "cpu") else np.asarray(page_table)
+        B = len(starts)
+        pos = starts[:, None] + np.arange(block)[None, :]
+        slots = table[np.arange(B)[:, None], pos // page_size] * page_size + pos % page_size
+        dev = pool.k.device
+        self.pool, self.plane, self.layer, self.block = pool, plane, layer, block
+        self.page_table = page_table if hasattr(page_table, "data_ptr") else \
+            torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(dev)
+        self.slots = torch.from_numpy(slots.reshape(-1).astype(np.int32)).to(dev)
+        self.cu = torch.from_numpy((np.arange(B + 1) * block).astype(np.int32)).to(dev)
+        ends = (starts + block).astype(np.int32)
+        self.seq = torch.from_numpy(ends).to(dev)
+        self.max_seq = int(ends.max())
+
+    def pass_(self, k, v, q, out=None, lse=None, with_lse: bool = True, scale=None, stream=None):
+        return extend(self.pool, self.plane, self.layer, k, v, self.slots, q, self.cu,
+                      self.page_table, self.seq, self.block, self.max_seq, scale=scale, out=out,
+                      lse=lse, with_lse=with_lse, stream=stream)

@@ -11,6 +11,8 @@
 // them in partition order (deterministic). Rows whose context fits one
 // partition are finished directly by the partial kernel, and the combine
 // kernel is launched only when some row can span several partitions.
+#include <algorithm>
+
 #include "folds.hpp"
 #include "launch.hpp"
 
@@ -21,9 +23,8 @@ namespace pkv {
 // a context's streaming rate grows with its waves: for GQA groups of 2, 8
 // waves let the longest contexts (which set the call's duration) finish
 // sooner (measured +6% over 4 on 64 requests of 512-2048 tokens). Such
-// workgroups fill a CU one at a time, so a call of many contexts runs in
-// rounds; small batches are then launched longest context first
-// (request_of_rank) and the short contexts fill in behind. A group of 1 has
+// workgroups fill a CU one at a time, so small batches run as persistent
+// workgroups that each take a balanced list of contexts (decode_whole). A group of 1 has
 // half the arithmetic per page and measured faster with 4 (+7% on 16
 // requests of 200-2000 tokens, 32 heads); larger groups need more than the
 // 256 registers a wave of an 8-wave workgroup may hold, so they use 4 too.
@@ -31,7 +32,7 @@ template <class F>
 constexpr int decode_waves() {
   return F::kGroup == 2 ? 8 : 4;
 }
-constexpr int kLptMaxBatch = 64;
+constexpr int kWholeMaxBatch = 64;  // requests decode_whole ranks (one per lane)
 
 // Combines partitions 0 .. np-1 of row `rowh` (in order) for output dim d.
 __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
@@ -53,21 +54,6 @@ __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
   }
 }
 
-// The request of rank q when requests are ordered longest context first (ties
-// by index); batch <= 64, one request per lane. Every lane returns it.
-__device__ __forceinline__ int request_of_rank(const int32_t *__restrict__ seq_lens, int batch,
-                                               int max_seq_len, int q) {
-  const int lane = threadIdx.x & 63;
-  const int mine = lane < batch ? min(max(seq_lens[lane], 0), max_seq_len) : -1;
-  int rank = 0;
-  for (int j = 0; j < batch; ++j) {
-    const int o = __builtin_amdgcn_readlane(mine, j);
-    rank += (o > mine) || (o == mine && j < lane);
-  }
-  const unsigned long long hit = __ballot(lane < batch && rank == q);
-  return hit ? __ffsll(hit) - 1 : 0;
-}
-
 // One workgroup per (partition j, kv head, request): its W waves take pages
 // w, w+W, ... of the partition, their states meet in LDS.
 template <typename E, class F, int W>
@@ -79,23 +65,13 @@ __global__ __launch_bounds__(64 * W) void decode_block(
     int32_t max_parts, typename E::storage *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc,
     const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
-    uint4 *kb_w, uint4 *vb_w, int32_t batch, int32_t lpt) {
+    uint4 *kb_w, uint4 *vb_w) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   constexpr int kThreads = 64 * W;
   __shared__ float2 lds_ml[W * G];
   __shared__ float lds_acc[W * G * D];
 
-  const int j = blockIdx.x;
-  int kvh = blockIdx.y, r = blockIdx.z;
-  if (lpt) {
-    // One partition per request (gridDim.x == 1), launched in (request, kv
-    // head) order: the i-th workgroup takes the i-th (request, kv head) of the
-    // longest-first order, so when workgroups run in more than one round the
-    // longest contexts start first and the short ones fill the gaps.
-    const int i = blockIdx.z * gridDim.y + blockIdx.y;
-    kvh = i % hkv;
-    r = request_of_rank(seq_lens, batch, max_seq_len, i / hkv);
-  }
+  const int j = blockIdx.x, kvh = blockIdx.y, r = blockIdx.z;
   const int n = min(max(seq_lens[r], 0), max_seq_len);
   const int np = min((n + partition - 1) / partition, max_parts);
   const int lo = j * partition;
@@ -145,6 +121,77 @@ __global__ __launch_bounds__(64 * W) void decode_block(
   }
 }
 
+// Whole contexts with persistent workgroups (batch <= 64, one request per
+// lane for the ranking). The (request, kv head) units are ranked longest
+// context first; workgroup k of M takes ranks k, 2M-1-k, 2M+k, 4M-1-k, ...
+// (a "snake" over the ranking), so each workgroup pairs a long context with
+// a short one and all carry nearly the same number of pages. A workgroup
+// starts its next unit as soon as the current one is written, instead of
+// leaving the compute unit to a new workgroup that must first fetch its
+// lengths, query and page ids. Each unit is folded exactly as decode_block
+// folds a whole context (same page interleave over the waves, same
+// wave-order merge), so the results are bitwise identical to it.
+template <typename E, class F, int W>
+__global__ __launch_bounds__(64 * W) void decode_whole(
+    const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
+    const typename E::storage *__restrict__ q, int32_t hq,
+    const int32_t *__restrict__ page_table, int32_t pt_stride,
+    const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
+    typename E::storage *__restrict__ out, float *__restrict__ lse,
+    const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
+    uint4 *kb_w, uint4 *vb_w) {
+  constexpr int G = F::kGroup, D = F::kHeadDim;
+  constexpr int kThreads = 64 * W;
+  __shared__ float2 lds_ml[W * G];
+  __shared__ float lds_acc[W * G * D];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Lane i < batch: the clamped length of request i and its rank in
+  // longest-first order (ties by index).
+  const int mine = lane < batch ? min(max(seq_lens[lane], 0), max_seq_len) : -1;
+  int rank = 0;
+  for (int j = 0; j < batch; ++j) {
+    const int o = __builtin_amdgcn_readlane(mine, j);
+    rank += (o > mine) || (o == mine && j < lane);
+  }
+  const int units = batch * hkv, M = gridDim.x, k = blockIdx.x;
+  for (int it = 0;; ++it) {
+    const int base = 2 * M * (it >> 1);
+    const int u = (it & 1) ? base + 2 * M - 1 - k : base + k;
+    if (u >= units) break;  // ranks grow with it
+    const int kvh = u % hkv;
+    const unsigned long long hit = __ballot(lane < batch && rank == u / hkv);
+    const int r = hit ? __ffsll(hit) - 1 : 0;
+    const int n = __builtin_amdgcn_readlane(mine, r);
+
+    F f(q + ((size_t)r * hq + (size_t)kvh * G) * D, qscale);
+    typename F::State st;
+    f.reset(st);
+    const int n_pages = (n + kPage - 1) / kPage;
+    const int npw = n_pages > w ? (n_pages - w + W - 1) / W : 0;
+    const int32_t *pt_row = page_table + (size_t)r * pt_stride;
+    if (k_new && n > 0) {
+      const int pa = (n - 1) / kPage;  // page of the newest token
+      if (pa % W == w)
+        f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
+                     n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
+    }
+    if (npw > 0) stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, w, npw, W, 0, n);
+    f.finish_wave(st);
+    emit_to_lds(f, st, w, lds_ml, lds_acc);
+    __syncthreads();
+    const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+      const int g = idx / D, d = idx % D;
+      float Mx, L, A;
+      combine_waves<G, D, W>(lds_ml, lds_acc, g, d, Mx, L, A);
+      finish<E>(out, lse, row0 + g, D, d, Mx, L, A);
+    }
+    __syncthreads();  // the next unit reuses the LDS
+  }
+}
+
 // Combine partitions 0 .. ceil(n / partition) - 1 of one (request, head)
 // row, in order. One thread per output dim.
 template <typename E>
@@ -169,6 +216,30 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
   using F = typename FoldFor<E, D, G>::type;
   const dim3 grid(a.max_parts, a.bank.num_kv_heads, a.batch);
   constexpr int W = decode_waves<F>();
+  if (a.max_parts == 1 && a.batch <= kWholeMaxBatch) {
+    // As many persistent workgroups as are resident at once (cached).
+    static int per_cu = 0;
+    if (per_cu == 0) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_whole<E, F, W>, 64 * W, 0) !=
+              hipSuccess ||
+          nb < 1)
+        nb = 1;
+      per_cu = nb;
+    }
+    const int units = a.batch * a.bank.num_kv_heads;
+    const int blocks = std::min(units, a.num_cus * per_cu);
+    hipLaunchKernelGGL((decode_whole<E, F, W>), dim3(blocks), dim3(64 * W), 0, stream,
+                       static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
+                       a.bank.num_pages, a.bank.num_kv_heads,
+                       static_cast<const typename E::storage *>(a.q), a.num_q_heads,
+                       a.page_table, a.pt_stride, a.seq_lens, a.batch, a.max_seq_len,
+                       a.scale * kLog2e, static_cast<typename E::storage *>(a.out), a.lse,
+                       static_cast<const typename E::storage *>(a.k_new),
+                       static_cast<const typename E::storage *>(a.v_new),
+                       static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((decode_block<E, F, W>), grid, dim3(64 * W), 0, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads,
@@ -177,8 +248,7 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
                      a.max_parts, static_cast<typename E::storage *>(a.out), a.lse, a.part_m,
                      a.part_l, a.part_acc, static_cast<const typename E::storage *>(a.k_new),
                      static_cast<const typename E::storage *>(a.v_new),
-                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v), a.batch,
-                     (a.max_parts == 1 && a.batch <= kLptMaxBatch) ? 1 : 0);
+                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, D, a.seq_lens, a.max_seq_len,

@@ -40,6 +40,7 @@ struct DecodeArgs {
   // seq_len - 1), [batch][num_kv_heads][head_dim], written and attended in
   // the same kernel. NULL: the pool already holds it.
   const void *k_new = nullptr, *v_new = nullptr;
+  int32_t num_cus = 256;  // compute units of the device (sizes persistent grids)
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -29,6 +29,13 @@ int ok() {
   return PKV_OK;
 }
 
+// Re-raises the current error with "call i" in front of its message.
+int fail_call(int code, int32_t i) {
+  char msg[sizeof g_err];
+  memcpy(msg, g_err, sizeof msg);
+  return fail(code, "call %d of the step: %s", i, msg);
+}
+
 constexpr int kDefaultPartition = 512;  // fixed partitions when the balanced split is off
 constexpr int kStreamMaxBatch = 4096;   // rows the balanced split indexes in LDS
 constexpr int kWholeMaxSeq = 4096;      // longest context one workgroup reads whole
@@ -239,6 +246,7 @@ int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const 
   a.lse = lse;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.num_cus = device_cus();
   char *ws = static_cast<char *>(workspace);
   if (stream_mode) {
     const int64_t nw = stream_wave_count(pool, batch, num_q_heads, max_seq_len);
@@ -282,6 +290,97 @@ int paged_decode_append_attn(const pkv_pool *pool, int32_t plane_id, int32_t lay
                      workspace, workspace_bytes, stream);
 }
 
+int paged_decode_step(const pkv_pool *pool, int32_t num_calls, const int32_t *plane_ids,
+                      const int32_t *layer_ids, const void *const *k_new,
+                      const void *const *v_new, const void *const *q, int32_t num_q_heads,
+                      const int32_t *page_table, int32_t page_table_stride,
+                      const int32_t *seq_lens, int32_t batch, int32_t max_seq_len, float scale,
+                      int32_t partition, void *const *out, float *const *lse, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (num_calls < 0) return fail(PKV_EINVAL, "num_calls %d < 0", num_calls);
+  if (num_calls == 0) return ok();
+  if (!plane_ids || !layer_ids || !q || !out)
+    return fail(PKV_EINVAL, "plane_ids / layer_ids / q / out is NULL");
+  if (!k_new != !v_new) return fail(PKV_EINVAL, "k_new and v_new must both be given or both NULL");
+  // Validate every call before enqueuing any (all or nothing).
+  for (int32_t i = 0; i < num_calls; ++i) {
+    pkv::Bank bank;
+    int rc = resolve_bank(pool, plane_ids[i], layer_ids[i], &bank);
+    if (rc) return fail_call(rc, i);
+    if (!q[i] || !out[i]) return fail(PKV_EINVAL, "call %d: q / out is NULL", i);
+    if (k_new && (!k_new[i] || !v_new[i]))
+      return fail(PKV_EINVAL, "call %d: k_new / v_new is NULL", i);
+    if (k_new && ((reinterpret_cast<uintptr_t>(k_new[i]) | reinterpret_cast<uintptr_t>(v_new[i])) & 15))
+      return fail(PKV_EINVAL, "call %d: k_new and v_new must be 16-byte aligned", i);
+  }
+  for (int32_t i = 0; i < num_calls; ++i) {
+    const int rc = decode_impl(pool, plane_ids[i], layer_ids[i], k_new ? k_new[i] : nullptr,
+                               v_new ? v_new[i] : nullptr, q[i], num_q_heads, page_table,
+                               page_table_stride, seq_lens, batch, max_seq_len, scale, partition,
+                               out[i], lse ? lse[i] : nullptr, workspace, workspace_bytes, stream);
+    if (rc) return fail_call(rc, i);
+  }
+  return ok();
+}
+
+struct pkv_step_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+int paged_decode_step_capture(const pkv_pool *pool, int32_t num_calls, const int32_t *plane_ids,
+                              const int32_t *layer_ids, const void *const *k_new,
+                              const void *const *v_new, const void *const *q,
+                              int32_t num_q_heads, const int32_t *page_table,
+                              int32_t page_table_stride, const int32_t *seq_lens, int32_t batch,
+                              int32_t max_seq_len, float scale, int32_t partition,
+                              void *const *out, float *const *lse, void *workspace,
+                              size_t workspace_bytes, void *capture_stream,
+                              pkv_step_graph **graph) {
+  if (!graph) return fail(PKV_EINVAL, "graph is NULL");
+  *graph = nullptr;
+  if (!capture_stream) return fail(PKV_EINVAL, "capture_stream must not be the null stream");
+  hipStream_t cs = static_cast<hipStream_t>(capture_stream);
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess)
+    return fail(PKV_ELAUNCH, "hipStreamBeginCapture failed");
+  int rc = paged_decode_step(pool, num_calls, plane_ids, layer_ids, k_new, v_new, q, num_q_heads,
+                             page_table, page_table_stride, seq_lens, batch, max_seq_len, scale,
+                             partition, out, lse, workspace, workspace_bytes, capture_stream);
+  char saved[sizeof g_err];
+  memcpy(saved, g_err, sizeof saved);
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(cs, &g);
+  if (rc) {
+    if (g) (void)hipGraphDestroy(g);
+    memcpy(g_err, saved, sizeof saved);
+    return rc;
+  }
+  if (e != hipSuccess || !g)
+    return fail(PKV_ELAUNCH, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  hipGraphExec_t x = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  if (ei != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(PKV_ELAUNCH, "hipGraphInstantiate failed: %s", hipGetErrorString(ei));
+  }
+  *graph = new pkv_step_graph{g, x};
+  return ok();
+}
+
+int paged_decode_step_graph_launch(pkv_step_graph *graph, void *stream) {
+  if (!graph) return fail(PKV_EINVAL, "graph is NULL");
+  const hipError_t e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ELAUNCH, "hipGraphLaunch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+void paged_decode_step_graph_destroy(pkv_step_graph *graph) {
+  if (!graph) return;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  delete graph;
+}
+
 int paged_decode_split_mode(const pkv_pool *pool, int32_t batch, int32_t num_q_heads,
                             int32_t max_seq_len, int32_t partition) {
   if (!pool || pool->num_kv_heads <= 0 || batch <= 0 || num_q_heads <= 0 || partition < 0)
@@ -312,11 +411,14 @@ int paged_decode_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads, int32
                   "paged_decode_reduce");
 }
 
-int paged_prefill_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
-                       int32_t num_q_heads, const int32_t *cu_q_lens, int32_t total_q,
-                       const int32_t *page_table, int32_t page_table_stride,
-                       const int32_t *seq_lens, int32_t batch, int32_t max_q_len,
-                       int32_t max_seq_len, float scale, void *out, float *lse, void *stream) {
+namespace {
+
+// Validates a prefill call and fills its launch arguments (nothing enqueued).
+int prefill_args(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
+                 int32_t num_q_heads, const int32_t *cu_q_lens, int32_t total_q,
+                 const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
+                 int32_t batch, int32_t max_q_len, int32_t max_seq_len, float scale, void *out,
+                 float *lse, pkv::PrefillArgs *a) {
   pkv::Bank bank;
   int rc = resolve_bank(pool, plane_id, layer_id, &bank);
   if (rc) return rc;
@@ -333,22 +435,57 @@ int paged_prefill_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
     return fail(PKV_EINVAL, "max_seq_len %d outside [0, stride * page_size]", max_seq_len);
   if (max_q_len < 0 || max_q_len > max_seq_len)
     return fail(PKV_EINVAL, "max_q_len %d outside [0, max_seq_len]", max_q_len);
-  pkv::PrefillArgs a{};
-  a.bank = bank;
-  a.q = q;
-  a.num_q_heads = num_q_heads;
-  a.cu_q_lens = cu_q_lens;
-  a.total_q = total_q;
-  a.page_table = page_table;
-  a.pt_stride = page_table_stride;
-  a.seq_lens = seq_lens;
-  a.batch = batch;
-  a.max_q_len = max_q_len;
-  a.max_seq_len = max_seq_len;
-  a.scale = scale;
-  a.out = out;
-  a.lse = lse;
+  *a = pkv::PrefillArgs{};
+  a->bank = bank;
+  a->q = q;
+  a->num_q_heads = num_q_heads;
+  a->cu_q_lens = cu_q_lens;
+  a->total_q = total_q;
+  a->page_table = page_table;
+  a->pt_stride = page_table_stride;
+  a->seq_lens = seq_lens;
+  a->batch = batch;
+  a->max_q_len = max_q_len;
+  a->max_seq_len = max_seq_len;
+  a->scale = scale;
+  a->out = out;
+  a->lse = lse;
+  return ok();
+}
+
+}  // namespace
+
+int paged_prefill_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
+                       int32_t num_q_heads, const int32_t *cu_q_lens, int32_t total_q,
+                       const int32_t *page_table, int32_t page_table_stride,
+                       const int32_t *seq_lens, int32_t batch, int32_t max_q_len,
+                       int32_t max_seq_len, float scale, void *out, float *lse, void *stream) {
+  pkv::PrefillArgs a;
+  int rc = prefill_args(pool, plane_id, layer_id, q, num_q_heads, cu_q_lens, total_q, page_table,
+                        page_table_stride, seq_lens, batch, max_q_len, max_seq_len, scale, out,
+                        lse, &a);
+  if (rc || total_q == 0) return rc;
   return launched(pkv::launch_prefill(a, static_cast<hipStream_t>(stream)), "paged_prefill_attn");
+}
+
+int paged_extend_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *k,
+                      const void *v, const int32_t *slot_mapping, const void *q,
+                      int32_t num_q_heads, const int32_t *cu_q_lens, int32_t total_q,
+                      const int32_t *page_table, int32_t page_table_stride,
+                      const int32_t *seq_lens, int32_t batch, int32_t max_q_len,
+                      int32_t max_seq_len, float scale, void *out, float *lse, void *stream) {
+  pkv::PrefillArgs a;
+  int rc = prefill_args(pool, plane_id, layer_id, q, num_q_heads, cu_q_lens, total_q, page_table,
+                        page_table_stride, seq_lens, batch, max_q_len, max_seq_len, scale, out,
+                        lse, &a);
+  if (rc || total_q == 0) return rc;
+  if (!k || !v || !slot_mapping) return fail(PKV_EINVAL, "k / v / slot_mapping is NULL");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+    return fail(PKV_EINVAL, "k and v must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launched(pkv::launch_kv_write(a.bank, k, v, slot_mapping, total_q, s), "paged_extend_attn");
+  if (rc) return rc;
+  return launched(pkv::launch_prefill(a, s), "paged_extend_attn");
 }
 
 const char *pkv_last_error(void) { return g_err; }

@@ -147,3 +147,8 @@ def sample_for_oracle(k_bank, v_bank, page_table: np.ndarray, seq_lens: np.ndarr
         for j, p in enumerate(need[i]):
             table[i, j] = remap[int(p)]
     return pool, table
+
+
+def say(*a):
+    """Names the case about to run (flushed, so a failing run shows it)."""
+    print(*a, file=sys.stderr, flush=True)

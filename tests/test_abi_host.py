@@ -158,3 +158,38 @@ def test_reduce_validation(L):
 def test_write_zero_tokens_is_noop(L):
     st, keep = _pool()
     assert L.paged_kv_write(ctypes.byref(st), 0, 0, None, None, None, 0, None) == pkv.PKV_OK
+
+
+def test_decode_step_validation(L):
+    # every call is validated before any is enqueued: a bad second call
+    # rejects the whole step, and the message names the call
+    st, keep = _pool(planes=3, layers=4, rec=(1, 2))
+    P = ctypes.c_void_p
+
+    def step(planes, layers, n=None, q_null=False, kv="both"):
+        n = len(planes) if n is None else n
+        pl = (ctypes.c_int32 * len(planes))(*planes)
+        ly = (ctypes.c_int32 * len(layers))(*layers)
+        ptrs = (P * len(planes))(*([None if q_null else FAKE] * len(planes)))
+        kn = ptrs if kv in ("both", "k") else None
+        vn = ptrs if kv == "both" else None
+        return L.paged_decode_step(ctypes.byref(st), n, pl, ly, kn, vn, ptrs, 4, FAKE, 4, FAKE,
+                                   2, 64, 1.0, 0, ptrs, None, FAKE, 1 << 30, None)
+
+    assert step([0, 2], [1, 0]) == pkv.PKV_ENOTHELD      # plane 2 does not hold layer 0
+    assert "call 1" in pkv.last_error()
+    assert step([0, 3], [1, 1]) == pkv.PKV_EINVAL        # plane 3 outside the pool
+    assert step([0], [0], q_null=True) == pkv.PKV_EINVAL
+    assert step([0], [0], kv="k") == pkv.PKV_EINVAL      # k_new without v_new
+    assert step([0], [0], n=-1) == pkv.PKV_EINVAL
+    assert step([], [], n=0) == pkv.PKV_OK               # nothing to do
+    handle = ctypes.c_void_p()
+    pl = (ctypes.c_int32 * 1)(0)
+    ptrs = (P * 1)(FAKE)
+    # capture needs a real (non-null) stream; nothing is recorded on failure
+    assert L.paged_decode_step_capture(ctypes.byref(st), 1, pl, pl, None, None, ptrs, 4, FAKE, 4,
+                                       FAKE, 2, 64, 1.0, 0, ptrs, None, FAKE, 1 << 30, None,
+                                       ctypes.byref(handle)) == pkv.PKV_EINVAL
+    assert not handle.value
+    assert L.paged_decode_step_graph_launch(None, None) == pkv.PKV_EINVAL
+    L.paged_decode_step_graph_destroy(None)  # a no-op

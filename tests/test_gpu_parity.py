@@ -130,6 +130,13 @@ DECODE_CASES = {
     # matrix-core fold, group 4, ragged lengths incl. odd page counts
     "bf16_d128_g4": dict(dtype="bf16", batch=7, seq_range=(1, 1500), num_q_heads=16,
                          num_kv_heads=4, head_dim=128),
+    # whole-context mode (64 x 8 (request, kv head) units) with persistent
+    # workgroups that take several contexts each: group 2 (vector fold) and
+    # group 8 (matrix-core fold)
+    "whole_g2": dict(dtype="bf16", batch=64, seq_range=(1, 400), num_q_heads=16,
+                     num_kv_heads=8, head_dim=128),
+    "whole_g8": dict(dtype="bf16", batch=64, seq_range=(1, 400), num_q_heads=64,
+                     num_kv_heads=8, head_dim=128),
 }
 
 
@@ -147,7 +154,7 @@ def test_decode_parity(name, seed):
 
 
 APPEND_CASES = ["c1_tiny_f32", "c2_ouro", "c3_huginn", "c5_longctx", "bf16_d128_g4",
-                "bf16_d64_g4"]
+                "bf16_d64_g4", "whole_g2", "whole_g8"]
 
 
 @pytest.mark.parametrize("partition", [0, 64])
@@ -185,6 +192,17 @@ def test_decode_edge_lengths(partition):
     ro, rl, _ = oracle_decode_case(case)
     out, lse, _ = gpu_decode_case(case, partition=partition)
     check(f"edge/p{partition}", "bf16", out, ro, rl, lse)
+    assert np.all(f64(out)[0] == 0) and np.all(f64(lse)[0] == -np.inf)
+
+
+def test_decode_edge_lengths_whole():
+    # the same edge lengths in whole-context mode (64 requests x 8 kv heads)
+    lens = [0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000] * 5 + [0, 2, 4095, 4096]
+    case = synth.make_decode_case(5, "bf16", len(lens), (0, 0), 16, 8, 128, seq_lens=lens)
+    assert pkv.split_mode(gpu_pool(case.layout), len(lens), 16, max(lens)) == "whole"
+    ro, rl, _ = oracle_decode_case(case)
+    out, lse, _ = gpu_decode_case(case)
+    check("edge/whole", "bf16", out, ro, rl, lse)
     assert np.all(f64(out)[0] == 0) and np.all(f64(lse)[0] == -np.inf)
 
 
