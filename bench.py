@@ -298,6 +298,59 @@ def run_prefill(reps=3, supplementary=True):
     return res
 
 
+def run_lotus(prompts=8, prompt_len=512, block=64, loop_iters=4, heads=32, D=128, reps=20):
+    """The LOTUS in-place loop: loop_iters + 1 passes over a fixed block of
+    `block` latent positions after each cached prompt, each pass one
+    paged_extend_attn (store_kv of the block to the same slots + extend-prefill
+    of all block rows). Reports the time per pass and per loop, and TFLOP/s of
+    4 * D * heads * (visible query-key pairs)."""
+    import torch
+
+    import paged_kv_attention_kvcache_amd as pkv
+    from paged_kv_attention_kvcache_amd import synth
+
+    rng = np.random.default_rng(0)
+    lens = np.full(prompts, prompt_len + block, np.int32)
+    table, num_pages, _ = synth.allocate_pages(rng, lens, 16)
+    bank_of, nb = pkv.bank_map(1, 1)
+    shape = (1, num_pages, heads, 16, D)
+    k = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), 11)
+    v = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), 12)
+    pool = pkv.Pool(torch.bfloat16, num_pages, heads, D, bank_of, nb, k=k, v=v)
+    lb = pkv.LotusBlock(pool, 0, 0, torch.from_numpy(table).cuda(), [prompt_len] * prompts,
+                        block)
+    rows = prompts * block
+    mk = lambda s_: synth.device_normal_(torch.empty((loop_iters + 1, rows, heads, D),
+                                                     dtype=torch.bfloat16, device="cuda"), s_)
+    kp, vp, qp = mk(13), mk(14), mk(15)
+    out = torch.empty((rows, heads, D), dtype=torch.bfloat16, device="cuda")
+
+    def loop():
+        for i in range(loop_iters + 1):
+            lb.pass_(kp[i], vp[i], qp[i], out=out, with_lse=False)
+
+    loop()
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        loop()
+    e.record()
+    torch.cuda.synchronize()
+    loop_s = a.elapsed_time(e) / 1e3 / reps
+    pairs = prompts * sum(prompt_len + j + 1 for j in range(block))
+    flops = 4 * D * heads * pairs * (loop_iters + 1)
+    res = {"prompts": prompts, "prompt_len": prompt_len, "block": block,
+           "loop_iters": loop_iters, "heads": heads, "head_dim": D,
+           "us_per_loop": round(loop_s * 1e6, 2),
+           "us_per_pass": round(loop_s * 1e6 / (loop_iters + 1), 2),
+           "TFLOPs": round(flops / loop_s / 1e12, 2),
+           "how": "paged_extend_attn per pass (store_kv to the block's fixed slots + "
+                  "extend-prefill of the block)"}
+    log(f"lotus: {res}")
+    return res
+
+
 # --------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(wl: DecodeWorkload, budget_s: float = 15.0):
@@ -490,14 +543,15 @@ def main():
         return
     log(f"device: {torch.cuda.get_device_name(0)}; workload {args.workload}")
     if args.prefill_only:
-        print(json.dumps({"prefill": run_prefill(supplementary=not args.no_supplementary)}),
-              flush=True)
+        print(json.dumps({"prefill": run_prefill(supplementary=not args.no_supplementary),
+                          "lotus": run_lotus()}), flush=True)
         return
     res, wl = run_decode(args)
     if not args.no_prefill:
         del wl
         torch.cuda.empty_cache()
         res["prefill"] = run_prefill(supplementary=not args.no_supplementary)
+        res["lotus"] = run_lotus()
     print(json.dumps(res), flush=True)
 
 

@@ -17,6 +17,9 @@ What it computes (the pages it follows are cited in ``oracle.h``):
   the work": page_table[request, position] -> slot).
 * ``decode_partials`` / ``combine`` -- the split-K partials and their combine
   (a rewriting of the same softmax, used to pin the reduction step).
+* ``lotus_loop`` -- the in-place latent loop: every pass hands the block's
+  fixed slots to store_kv again (an overwrite) and runs one extend-prefill
+  over all block positions ("Faster fuzzy minds", section "LOTUS").
 
 Arrays: bf16 data travels as ``np.uint16`` raw bits, fp32 as ``np.float32``.
 """
@@ -260,3 +263,20 @@ def combine(n_parts, pm: np.ndarray, pl: np.ndarray, pacc: np.ndarray, lib=None)
 def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
     """Exact decode of bf16 raw bits (for tests)."""
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def lotus_loop(pool: Pool, plane: int, layer: int, passes, block_slots, cu_q_lens, page_table,
+               seq_lens, scale: float | None = None, lib=None, after_pass=None):
+    """LOTUS ("Faster fuzzy minds", section "LOTUS"): the block's slots are
+    chosen once; each pass (k, v, q) writes its K/V to those same slots,
+    overwriting the previous pass, then runs one extend-prefill of all block
+    rows (query row j of request r at position seq_lens[r] - q_len + j) over
+    the prefix and the block. Returns [(out, lse)] per pass. after_pass(i) is
+    called after pass i's write and attention (for inspection)."""
+    res = []
+    for i, (k, v, q) in enumerate(passes):
+        kv_write(pool, plane, layer, k, v, block_slots, lib)
+        res.append(prefill(pool, plane, layer, q, cu_q_lens, page_table, seq_lens, scale, lib))
+        if after_pass is not None:
+            after_pass(i)
+    return res

@@ -374,6 +374,50 @@ def prefix_writes(case: PrefillCase, upto: Sequence[int]):
     return np.concatenate(ks), np.concatenate(vs), np.concatenate(ss).astype(np.int32)
 
 
+@dataclasses.dataclass
+class LotusCase:
+    """A latent block of `block` positions after each request's prompt, run
+    for several passes: the prompt's K/V are written once; every pass brings
+    new K/V and Q for the block's rows (request-major, packed)."""
+
+    layout: Layout
+    num_q_heads: int
+    prompt_lens: np.ndarray  # [B]
+    block: int
+    page_table: np.ndarray   # [B, stride], room for prompt + block
+    prompt_k: list           # per request [prompt, Hkv, D]
+    prompt_v: list
+    prompt_slots: np.ndarray  # [sum prompt] slots of the prompt tokens, request-major
+    block_slots: np.ndarray  # [B * block] slots of the block positions (fixed)
+    passes: list             # per pass (k [B*block, Hkv, D], v, q [B*block, Hq, D])
+
+
+def make_lotus_case(seed: int, dtype: str, prompt_lens: Sequence[int], block: int,
+                    num_passes: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    page_size: int = 16, q_scale: float = 1.0) -> LotusCase:
+    rng = np.random.default_rng(seed)
+    prompt_lens = np.asarray(prompt_lens, np.int32)
+    B = len(prompt_lens)
+    total = prompt_lens + block
+    page_table, num_pages, _ = allocate_pages(rng, total, page_size)
+    layout = Layout(dtype, page_size, num_pages, num_kv_heads, head_dim)
+    pk, pv, ps, bs = [], [], [], []
+    for r in range(B):
+        n = int(prompt_lens[r])
+        pk.append(draw(rng, (n, num_kv_heads, head_dim), dtype))
+        pv.append(draw(rng, (n, num_kv_heads, head_dim), dtype))
+        ps.append(slots_of(page_table, r, np.arange(n), page_size))
+        bs.append(slots_of(page_table, r, np.arange(n, n + block), page_size))
+    passes = []
+    for _ in range(num_passes):
+        passes.append((draw(rng, (B * block, num_kv_heads, head_dim), dtype),
+                       draw(rng, (B * block, num_kv_heads, head_dim), dtype),
+                       draw(rng, (B * block, num_q_heads, head_dim), dtype, q_scale)))
+    return LotusCase(layout, num_q_heads, prompt_lens, block, page_table, pk, pv,
+                     np.concatenate(ps).astype(np.int32), np.concatenate(bs).astype(np.int32),
+                     passes)
+
+
 def device_normal_(t, seed: int, scale: float = 1.0):
     """Fill a device tensor in place with N(0, scale^2) from a seeded torch
     generator on its device (for pools too large to draw on the host)."""
