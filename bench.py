@@ -351,6 +351,39 @@ def run_lotus(prompts=8, prompt_len=512, block=64, loop_iters=4, heads=32, D=128
     return res
 
 
+def run_page_mgr(reps=200):
+    """Host bookkeeping of the page manager for one Huginn-shaped decode step
+    (16 requests, 132 bank writes of one token each, then a publication
+    check of every request's page-table row over 32 planes), and the cost
+    of allocating and releasing pages."""
+    import paged_kv_attention_kvcache_amd as pkv
+
+    bank_of, _ = pkv.bank_map(32, 8, 2, 4)
+    order = [(0, 0), (0, 1)] + [(t, l) for t in range(32) for l in range(2, 6)] + \
+            [(0, 6), (0, 7)]
+    B, pages_per_req = 16, 126  # 2000-token prompts
+    m = pkv.PageManager(B * pages_per_req + 64, bank_of)
+    rows = [m.alloc(pages_per_req) for _ in range(B)]
+    slots = np.array([r[-1] * 16 + 3 for r in rows], np.int32)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for (p, l) in order:
+            m.note_write(p, l, slots)
+        for r in rows:
+            m.published_prefix(32, r)
+    step_us = (time.perf_counter() - t0) / reps * 1e6
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ids = m.alloc(64)
+        m.release(ids)
+    pair_us = (time.perf_counter() - t0) / reps * 1e6
+    m.close()
+    return {"host_us_per_huginn_step": round(step_us, 2),
+            "host_us_alloc_release_64_pages": round(pair_us, 2),
+            "how": "pkv_mgr_note_write per bank call + pkv_mgr_published_prefix per request, "
+                   "through the Python binding (host only)"}
+
+
 # --------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(wl: DecodeWorkload, budget_s: float = 15.0):
@@ -552,6 +585,7 @@ def main():
         torch.cuda.empty_cache()
         res["prefill"] = run_prefill(supplementary=not args.no_supplementary)
         res["lotus"] = run_lotus()
+    res["page_manager"] = run_page_mgr()
     print(json.dumps(res), flush=True)
 
 

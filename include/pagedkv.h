@@ -69,7 +69,8 @@ enum {
   PKV_EUNSUPPORTED = -2,  /* dtype / head_dim / page_size / group size  */
   PKV_ENOTHELD = -3,      /* (plane, layer) owns no bank                */
   PKV_EWORKSPACE = -4,    /* workspace too small                        */
-  PKV_ELAUNCH = -5        /* a kernel launch failed                     */
+  PKV_ELAUNCH = -5,       /* a kernel launch failed                     */
+  PKV_ENOSPACE = -6       /* page manager: not enough free pages        */
 };
 
 /* The pool descriptor. dtype is shared by the pool, q, k/v inputs and out.
@@ -289,6 +290,51 @@ int paged_extend_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, 
                       const int32_t *page_table, int32_t page_table_stride,
                       const int32_t *seq_lens, int32_t batch, int32_t max_q_len,
                       int32_t max_seq_len, float scale, void *out, float *lse, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Host page manager (no device work). One page-id space serves every bank
+ * ([FFM] "When scheduler does the work": slots are addressed through a page
+ * table and sequences may share them; a shared prefix is inherited). Pages
+ * carry reference counts -- a page is free again when its last reference is
+ * released -- and the free count is O(1) ([PR152] "Notes" #151). A page may
+ * be published as a reusable prefix page once every one of its slots has
+ * been written in every layer that each plane in use holds ([PR152]
+ * "Summary": coverage is checked per plane over the layers it holds, all
+ * layers at depth 0 and the recurrent layers deeper). Not thread-safe: one
+ * manager per scheduler thread. */
+typedef struct pkv_page_mgr pkv_page_mgr;
+
+/* A manager of num_pages pages of page_size slots (<= 64) for the plane map
+ * bank_of [num_planes * num_layers] (HOST, copied; -1 = not held; each bank
+ * id at most once). Every page starts free. NULL on invalid arguments. */
+pkv_page_mgr *pkv_mgr_create(int32_t num_pages, int32_t page_size, int32_t num_planes,
+                             int32_t num_layers, const int32_t *bank_of);
+void pkv_mgr_destroy(pkv_page_mgr *mgr);
+/* Free pages (constant time), or PKV_EINVAL for a NULL manager. */
+int32_t pkv_mgr_free_count(const pkv_page_mgr *mgr);
+/* Takes n free pages into page_ids[n] (HOST), each with one reference and no
+ * slot marked written; all or nothing (PKV_ENOSPACE when fewer are free). */
+int pkv_mgr_alloc(pkv_page_mgr *mgr, int32_t n, int32_t *page_ids);
+/* One more reference to each listed page (a request that aliases a shared
+ * prefix page); every page must be in use. All or nothing. */
+int pkv_mgr_retain(pkv_page_mgr *mgr, int32_t n, const int32_t *page_ids);
+/* Drops one reference per listed entry (an id may repeat); a page whose
+ * count reaches 0 is free. All or nothing: no page may be released more
+ * times than it is held. */
+int pkv_mgr_release(pkv_page_mgr *mgr, int32_t n, const int32_t *page_ids);
+/* References held on page (0 = free), or PKV_EINVAL. */
+int32_t pkv_mgr_refcount(const pkv_page_mgr *mgr, int32_t page);
+/* Records that store_kv wrote these slots (HOST [n], the slot_mapping of a
+ * paged_kv_write; negative = padding, skipped) in bank (plane, layer).
+ * PKV_ENOTHELD if the plane does not hold the layer; PKV_EINVAL for a slot
+ * at or past num_pages * page_size (nothing recorded then). */
+int pkv_mgr_note_write(pkv_page_mgr *mgr, int32_t plane, int32_t layer, int32_t n,
+                       const int32_t *slots);
+/* The number of leading pages of page_ids [n_pages] (a request's page-table
+ * row) that may be published: in use, and every slot written in every layer
+ * held by each of planes 0 .. planes_used - 1. Negative on invalid arguments. */
+int32_t pkv_mgr_published_prefix(const pkv_page_mgr *mgr, int32_t planes_used,
+                                 const int32_t *page_ids, int32_t n_pages);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *pkv_last_error(void);

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 
 PKV_F32, PKV_BF16 = 0, 1
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOTHELD, PKV_EWORKSPACE, PKV_ELAUNCH = 0, -1, -2, -3, -4, -5
+PKV_ENOSPACE = -6
 DEFAULT_PARTITION = 512
 
 _lib = None
@@ -53,7 +54,9 @@ EXPORTS = ("pkv_bank_map", "pkv_pool_bytes", "paged_kv_write", "paged_decode_wor
            "paged_decode_attn", "paged_decode_append_attn", "paged_decode_split_mode",
            "paged_decode_step", "paged_decode_step_capture", "paged_decode_step_graph_launch",
            "paged_decode_step_graph_destroy", "paged_decode_reduce", "paged_prefill_attn",
-           "paged_extend_attn", "pkv_last_error")
+           "paged_extend_attn", "pkv_mgr_create", "pkv_mgr_destroy", "pkv_mgr_free_count",
+           "pkv_mgr_alloc", "pkv_mgr_retain", "pkv_mgr_release", "pkv_mgr_refcount",
+           "pkv_mgr_note_write", "pkv_mgr_published_prefix", "pkv_last_error")
 
 
 def lib():
@@ -98,6 +101,21 @@ def lib():
         L.paged_extend_attn.argtypes = [P, i32, i32, P, P, P, P, i32, P, i32, P, i32, P, i32,
                                         i32, i32, ctypes.c_float, P, P, P]
         L.paged_extend_attn.restype = ctypes.c_int
+        L.pkv_mgr_create.argtypes = [i32, i32, i32, i32, P]
+        L.pkv_mgr_create.restype = P
+        L.pkv_mgr_destroy.argtypes = [P]
+        L.pkv_mgr_destroy.restype = None
+        L.pkv_mgr_free_count.argtypes = [P]
+        L.pkv_mgr_free_count.restype = i32
+        for name in ("pkv_mgr_alloc", "pkv_mgr_retain", "pkv_mgr_release"):
+            getattr(L, name).argtypes = [P, i32, P]
+            getattr(L, name).restype = ctypes.c_int
+        L.pkv_mgr_refcount.argtypes = [P, i32]
+        L.pkv_mgr_refcount.restype = i32
+        L.pkv_mgr_note_write.argtypes = [P, i32, i32, i32, P]
+        L.pkv_mgr_note_write.restype = ctypes.c_int
+        L.pkv_mgr_published_prefix.argtypes = [P, i32, P, i32]
+        L.pkv_mgr_published_prefix.restype = i32
         L.pkv_last_error.argtypes = []
         L.pkv_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -414,3 +432,59 @@ class LotusBlock:
         return extend(self.pool, self.plane, self.layer, k, v, self.slots, q, self.cu,
                       self.page_table, self.seq, self.block, self.max_seq, scale=scale, out=out,
                       lse=lse, with_lse=with_lse, stream=stream)
+
+
+class PageManager:
+    """Host page manager of a multi-plane pool (pkv_mgr_*): reference-counted
+    pages, a constant-time free count, and per-plane prefix publication."""
+
+    def __init__(self, num_pages: int, bank_of: np.ndarray, page_size: int = 16):
+        self.bank_of = np.ascontiguousarray(bank_of, dtype=np.int32)
+        planes, layers = self.bank_of.shape
+        self._h = lib().pkv_mgr_create(num_pages, page_size, planes, layers,
+                                       self.bank_of.ctypes.data)
+        if not self._h:
+            raise PagedKVError(PKV_EINVAL, "pkv_mgr_create: invalid arguments")
+
+    @staticmethod
+    def _ids(ids) -> np.ndarray:
+        return np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+
+    def free_count(self) -> int:
+        return int(_check(lib().pkv_mgr_free_count(self._h)))
+
+    def alloc(self, n: int) -> np.ndarray:
+        out = np.empty(n, np.int32)
+        _check(lib().pkv_mgr_alloc(self._h, n, out.ctypes.data))
+        return out
+
+    def retain(self, ids) -> None:
+        a = self._ids(ids)
+        _check(lib().pkv_mgr_retain(self._h, len(a), a.ctypes.data))
+
+    def release(self, ids) -> None:
+        a = self._ids(ids)
+        _check(lib().pkv_mgr_release(self._h, len(a), a.ctypes.data))
+
+    def refcount(self, page: int) -> int:
+        return int(_check(lib().pkv_mgr_refcount(self._h, page)))
+
+    def note_write(self, plane: int, layer: int, slots) -> None:
+        a = self._ids(slots)
+        _check(lib().pkv_mgr_note_write(self._h, plane, layer, len(a), a.ctypes.data))
+
+    def published_prefix(self, planes_used: int, page_ids) -> int:
+        a = self._ids(page_ids)
+        return int(_check(lib().pkv_mgr_published_prefix(self._h, planes_used, a.ctypes.data,
+                                                         len(a))))
+
+    def close(self) -> None:
+        if self._h:
+            lib().pkv_mgr_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -7,6 +7,9 @@
 
 namespace pkv {
 
+// Sets the thread's last-error message (pkv_last_error) and returns code.
+int set_error(int code, const char *msg);
+
 // One bank of the pool: K and V base pointers already offset to the bank.
 struct Bank {
   void *k;

@@ -140,6 +140,11 @@ int launched(hipError_t e, const char *what) {
 
 }  // namespace
 
+int pkv::set_error(int code, const char *msg) {
+  snprintf(g_err, sizeof g_err, "%s", msg);
+  return code;
+}
+
 extern "C" {
 
 int pkv_bank_map(int32_t num_planes, int32_t num_layers, int32_t rec_first, int32_t rec_count,

@@ -1,0 +1,175 @@
+"""The host page manager (pkv_mgr_*) against the plain model in
+oracle/pagemgr.py, and the model pinned to what the pages state.
+
+Pins of the model:
+* vllm-rlt pull 152, "Summary": with Huginn's map (plane 0 holds all 8
+  layers, deeper planes the 4 recurrent ones) a page written in every layer
+  each plane holds is published under the per-plane rule, while the rule the
+  pull replaced (every layer of every plane) never publishes it;
+* the same section: for a fully recurrent model (Ouro: every plane holds
+  every layer) the two rules agree;
+* a page with one slot missing in one held layer is not published, nor is
+  anything after it (a prefix is contiguous);
+* reference counts: a page is free exactly when its last holder releases it.
+
+Parity: seeded random sequences of operations (invalid ones included) give
+the same results, step by step, on the library and on the model.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_kvcache_amd as pkv
+from oracle.pagemgr import PageModel
+
+P = 16
+
+
+def huginn_map():
+    return pkv.bank_map(32, 8, 2, 4)[0]
+
+
+def ouro_map():
+    return pkv.bank_map(4, 24)[0]
+
+
+def write_page(m, bank_of, planes, page, skip=None):
+    """Write every slot of `page` in every layer each of `planes` holds."""
+    for p in planes:
+        for layer in range(bank_of.shape[1]):
+            if bank_of[p][layer] < 0:
+                continue
+            slots = [page * P + o for o in range(P) if skip != (p, layer, o)]
+            m.note_write(p, layer, slots)
+
+
+def test_model_huginn_per_plane_publication():
+    bank_of = huginn_map()
+    m = PageModel(8, P, bank_of)
+    ids = m.alloc(3)
+    for page in ids:
+        write_page(m, bank_of, range(32), page)
+    assert m.published_prefix(32, ids) == 3
+    # plane >= 1 never writes the prelude / coda layers: the old rule never publishes
+    assert m.published_prefix(32, ids, rule="every_layer") == 0
+    assert m.published_prefix(1, ids, rule="every_layer") == 3  # depth 0 holds every layer
+
+
+def test_model_fully_recurrent_rules_agree():
+    bank_of = ouro_map()
+    rng = np.random.default_rng(3)
+    m = PageModel(6, P, bank_of)
+    ids = m.alloc(6)
+    for _ in range(400):
+        p, layer, page = rng.integers(4), rng.integers(24), rng.choice(ids)
+        m.note_write(p, layer, page * P + rng.integers(0, P, size=rng.integers(1, 17)))
+    for page in ids[:3]:
+        write_page(m, bank_of, range(4), page)
+    for used in range(1, 5):
+        for start in range(6):
+            row = list(ids[start:]) + list(ids[:start])
+            assert m.published_prefix(used, row) == m.published_prefix(used, row, "every_layer")
+
+
+def test_model_missing_slot_stops_the_prefix():
+    bank_of = huginn_map()
+    m = PageModel(4, P, bank_of)
+    ids = m.alloc(4)
+    for i, page in enumerate(ids):
+        write_page(m, bank_of, range(32), page, skip=(17, 4, 9) if i == 1 else None)
+    assert m.published_prefix(32, ids) == 1
+    assert m.published_prefix(18, ids) == 1
+    assert m.published_prefix(17, ids) == 4  # planes 0..16 in use: plane 17 does not count
+
+
+def test_model_refcounts():
+    m = PageModel(4, P, huginn_map())
+    a = m.alloc(2)
+    assert a == [0, 1] and m.free_count() == 2
+    assert m.retain([a[0]]) and m.refs[a[0]] == 2
+    assert m.release([a[0]]) and m.free_count() == 2
+    assert m.release([a[0], a[1]]) and m.free_count() == 4
+    assert not m.release([a[0]])
+    assert m.alloc(5) is None
+
+
+@pytest.mark.parametrize("mapname", ["huginn", "ouro"])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_library_matches_model(mapname, seed):
+    bank_of = huginn_map() if mapname == "huginn" else ouro_map()
+    planes, layers = bank_of.shape
+    N = 24
+    lib = pkv.PageManager(N, bank_of, P)
+    mod = PageModel(N, P, bank_of)
+    rng = np.random.default_rng(seed)
+    rows = []  # page-table rows handed out so far
+
+    def both(fn_lib, fn_mod):
+        try:
+            got = fn_lib()
+            ok_lib = True
+        except pkv.PagedKVError:
+            got, ok_lib = None, False
+        want = fn_mod()
+        ok_mod = want is not None and want is not False
+        assert ok_lib == ok_mod
+        return got, want
+
+    for step in range(600):
+        op = rng.integers(7)
+        if op == 0:
+            n = int(rng.integers(0, 8))
+            got, want = both(lambda: lib.alloc(n), lambda: mod.alloc(n))
+            if got is not None:
+                assert list(got) == list(want)
+                rows.append(list(got))
+        elif op == 1 and rows:
+            row = rows[rng.integers(len(rows))]
+            ids = list(rng.choice(row, size=rng.integers(1, len(row) + 1))) if row else []
+            both(lambda: lib.retain(ids) or True, lambda: mod.retain(ids))
+        elif op == 2:
+            ids = list(rng.integers(0, N, size=rng.integers(0, 4)))
+            both(lambda: lib.release(ids) or True, lambda: mod.release(ids))
+        elif op == 3 and rows:
+            row = rows[rng.integers(len(rows))]
+            if row:
+                p, layer = int(rng.integers(planes)), int(rng.integers(layers))
+                page = int(rng.choice(row))
+                slots = list(page * P + rng.integers(0, P, size=rng.integers(1, 2 * P)))
+                slots += [-1] * int(rng.integers(0, 2))
+                both(lambda: lib.note_write(p, layer, slots) or True,
+                     lambda: mod.note_write(p, layer, slots))
+        elif op == 4 and rows:
+            row = rows[rng.integers(len(rows))]
+            for page in row:  # a whole page written on every plane
+                write_page(lib, bank_of, range(planes), page)
+                write_page(mod, bank_of, range(planes), page)
+        elif op == 5 and rows:
+            row = rows[rng.integers(len(rows))]
+            used = int(rng.integers(1, planes + 1))
+            assert lib.published_prefix(used, row) == mod.published_prefix(used, row)
+        assert lib.free_count() == mod.free_count()
+        for page in range(N):
+            assert lib.refcount(page) == mod.refs.get(page, 0)
+    lib.close()
+
+
+def test_library_errors():
+    bank_of = huginn_map()
+    m = pkv.PageManager(4, bank_of, P)
+    with pytest.raises(pkv.PagedKVError) as e:
+        m.alloc(5)
+    assert e.value.code == pkv.PKV_ENOSPACE and m.free_count() == 4
+    ids = m.alloc(2)
+    with pytest.raises(pkv.PagedKVError) as e:
+        m.note_write(3, 0, [ids[0] * P])  # plane 3 holds only layers 2..5
+    assert e.value.code == pkv.PKV_ENOTHELD
+    with pytest.raises(pkv.PagedKVError):
+        m.note_write(0, 0, [4 * P])  # slot outside the pool
+    with pytest.raises(pkv.PagedKVError):
+        m.release([ids[0], ids[0]])  # held once, released twice: nothing released
+    assert m.refcount(ids[0]) == 1
+    with pytest.raises(pkv.PagedKVError):
+        m.retain([3])  # a free page
+    m.close()
