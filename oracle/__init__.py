@@ -17,6 +17,9 @@ What it computes (the pages it follows are cited in ``oracle.h``):
   the work": page_table[request, position] -> slot).
 * ``decode_partials`` / ``combine`` -- the split-K partials and their combine
   (a rewriting of the same softmax, used to pin the reduction step).
+* ``decode_latest`` -- decode with early exit: each position is read from the
+  deepest plane it holds, up to the query's plane ("Faster fuzzy minds",
+  section "Can we actually stop early?").
 * ``lotus_loop`` -- the in-place latent loop: every pass hands the block's
   fixed slots to store_kv again (an overwrite) and runs one extend-prefill
   over all block positions ("Faster fuzzy minds", section "LOTUS").
@@ -88,8 +91,10 @@ def _bind(lib):
     lib.orc_decode_partials.argtypes = [P, i32, i32, P, i32, P, i32, P, i32,
                                         ctypes.c_double, i32, i32, P, P, P]
     lib.orc_combine.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+    lib.orc_decode_latest.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, P, i32,
+                                      ctypes.c_double, P, P]
     for f in (lib.orc_bank_map, lib.orc_kv_write, lib.orc_attend,
-              lib.orc_decode_partials, lib.orc_combine):
+              lib.orc_decode_partials, lib.orc_combine, lib.orc_decode_latest):
         f.restype = ctypes.c_int
     return lib
 
@@ -219,6 +224,29 @@ def prefill(pool: Pool, plane: int, layer: int, q: np.ndarray, cu_q_lens, page_t
             seq_lens, scale: float | None = None, lib=None):
     """Packed q [sum q_len, Hq, D] -> (out, lse) in fp64."""
     return _attend(pool, plane, layer, q, cu_q_lens, page_table, seq_lens, scale, lib)
+
+
+def decode_latest(pool: Pool, plane: int, layer: int, exit_depth, q: np.ndarray, page_table,
+                  seq_lens, scale: float | None = None, lib=None):
+    """Early-exit decode ("Faster fuzzy minds", section "Can we actually stop
+    early?"): position pos of request r is read from plane
+    min(plane, exit_depth[r, pos]) of the same layer. exit_depth int8
+    [B, stride >= max seq_len]. Returns (out, lse) in fp64."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=pool.np_dtype)
+    B, Hq, D = q.shape
+    page_table = _i32(page_table)
+    seq_lens = _i32(seq_lens)
+    ed = np.ascontiguousarray(exit_depth, dtype=np.int8)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.zeros((B, Hq, D), np.float64)
+    lse = np.zeros((B, Hq), np.float64)
+    st = pool._struct()
+    _check(lib.orc_decode_latest(ctypes.byref(st), plane, layer, _ptr(ed), ed.shape[1], _ptr(q),
+                                 Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B,
+                                 float(scale), _ptr(out), _ptr(lse)), "decode_latest")
+    return out, lse
 
 
 def decode_partials(pool: Pool, plane: int, layer: int, q: np.ndarray, page_table,

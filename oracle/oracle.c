@@ -150,11 +150,20 @@ static int check_tables(const orc_pool *p, const int32_t *page_table,
 
 /* Gather positions [0, n) of kv head kvh of request r into contiguous
  * Kc[n][D], Vc[n][D] (fp64): position pos lives at page pt[r][pos / P],
- * offset pos % P. */
-static void gather(const orc_pool *p, int32_t bank, const int32_t *pt_row,
-                   int32_t kvh, int32_t n, double *Kc, double *Vc) {
+ * offset pos % P, of bank `bank` -- or, given the request's exit depths
+ * (early-exit decode), of the bank of (min(plane, depth[pos]), layer).
+ * Returns 0 or an error code. */
+static int gather(const orc_pool *p, int32_t bank, const int8_t *depth,
+                  int32_t plane, int32_t layer, const int32_t *pt_row,
+                  int32_t kvh, int32_t n, double *Kc, double *Vc) {
   int32_t D = p->head_dim;
   for (int32_t pos = 0; pos < n; ++pos) {
+    if (depth) {
+      int32_t e = depth[pos];
+      if (e < 0 || e >= p->num_planes) return ORC_EINVAL;
+      bank = bank_for(p, e < plane ? e : plane, layer);
+      if (bank < 0) return bank;
+    }
     int32_t page = pt_row[pos / p->page_size];
     int32_t off = pos % p->page_size;
     for (int32_t d = 0; d < D; ++d) {
@@ -163,6 +172,7 @@ static void gather(const orc_pool *p, int32_t bank, const int32_t *pt_row,
       Vc[(size_t)pos * D + d] = load_elem(p->elem_bytes, p->v, i);
     }
   }
+  return ORC_OK;
 }
 
 /* Textbook softmax attention of one query over keys [lo, hi) of the gathered
@@ -236,7 +246,7 @@ int orc_attend(const orc_pool *p, int32_t plane, int32_t layer,
 #pragma omp atomic write
       failed = 1;
     } else {
-      gather(p, bank, page_table + (size_t)r * pt_stride, kvh, n, Kc, Vc);
+      gather(p, bank, NULL, plane, layer, page_table + (size_t)r * pt_stride, kvh, n, Kc, Vc);
       for (int32_t j = 0; j < qlen; ++j) {
         /* Query row j sits at position n - qlen + j and sees keys 0..pos. */
         int32_t pos = n - qlen + j;
@@ -254,6 +264,60 @@ int orc_attend(const orc_pool *p, int32_t plane, int32_t layer,
     free(Kc); free(Vc); free(w); free(qv); free(acc);
   }
   return failed ? ORC_EINVAL : ORC_OK;
+}
+
+int orc_decode_latest(const orc_pool *p, int32_t plane, int32_t layer,
+                      const int8_t *exit_depth, int32_t exit_stride,
+                      const void *q, int32_t Hq,
+                      const int32_t *page_table, int32_t pt_stride,
+                      const int32_t *seq_lens, int32_t batch, double scale,
+                      double *out, double *lse) {
+  int rc = check_pool(p);
+  if (rc) return rc;
+  if (batch < 0 || Hq <= 0 || Hq % p->num_kv_heads != 0 || pt_stride < 0)
+    return ORC_EINVAL;
+  if (batch == 0) return ORC_OK;
+  if (!q || !page_table || !seq_lens || !out || !lse || !exit_depth) return ORC_EINVAL;
+  int bank = bank_for(p, plane, layer);
+  if (bank < 0) return bank;
+  rc = check_tables(p, page_table, pt_stride, seq_lens, batch, NULL);
+  if (rc) return rc;
+  for (int32_t r = 0; r < batch; ++r)
+    if (seq_lens[r] > exit_stride) return ORC_ELEN;
+
+  const int32_t D = p->head_dim, Hkv = p->num_kv_heads, G = Hq / Hkv;
+  const int32_t pairs = batch * Hkv;
+  int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int32_t pr = 0; pr < pairs; ++pr) {
+    int32_t r = pr / Hkv, kvh = pr % Hkv;
+    int32_t n = seq_lens[r];
+    size_t nn = (size_t)(n > 0 ? n : 1);
+    double *Kc = (double *)malloc(nn * D * sizeof(double));
+    double *Vc = (double *)malloc(nn * D * sizeof(double));
+    double *w = (double *)malloc(nn * sizeof(double));
+    double *qv = (double *)malloc((size_t)D * sizeof(double));
+    double *acc = (double *)malloc((size_t)D * sizeof(double));
+    int err = (!Kc || !Vc || !w || !qv || !acc) ? ORC_EINVAL : ORC_OK;
+    if (!err)
+      err = gather(p, bank, exit_depth + (size_t)r * exit_stride, plane, layer,
+                   page_table + (size_t)r * pt_stride, kvh, n, Kc, Vc);
+    if (err) {
+#pragma omp critical
+      failed = failed ? failed : err;
+    } else {
+      for (int32_t g = 0; g < G; ++g) {
+        int32_t h = kvh * G + g;
+        size_t qo = ((size_t)r * Hq + h) * D;
+        for (int32_t d = 0; d < D; ++d) qv[d] = load_elem(p->elem_bytes, q, qo + d);
+        double m, l;
+        attend_span(qv, Kc, Vc, 0, n, D, scale, w, &m, &l, acc, out + qo,
+                    lse + (size_t)r * Hq + h);
+      }
+    }
+    free(Kc); free(Vc); free(w); free(qv); free(acc);
+  }
+  return failed;
 }
 
 int orc_decode_partials(const orc_pool *p, int32_t plane, int32_t layer,
@@ -292,7 +356,7 @@ int orc_decode_partials(const orc_pool *p, int32_t plane, int32_t layer,
 #pragma omp atomic write
       failed = 1;
     } else {
-      gather(p, bank, page_table + (size_t)r * pt_stride, kvh, n, Kc, Vc);
+      gather(p, bank, NULL, plane, layer, page_table + (size_t)r * pt_stride, kvh, n, Kc, Vc);
       for (int32_t g = 0; g < G; ++g) {
         int32_t h = kvh * G + g;
         size_t qo = ((size_t)r * Hq + h) * D;

@@ -90,6 +90,21 @@ int orc_attend(const orc_pool *pool, int32_t plane, int32_t layer,
                const int32_t *seq_lens, int32_t batch, double scale,
                double *out, double *lse);
 
+/* Decode with early exit ([FFM] "Can we actually stop early?": a token that
+ * halts at an earlier depth keeps its last, converged KV, and later tokens
+ * attend that latest bank). exit_depth[r * exit_stride + pos] is the deepest
+ * plane position pos of request r holds; the query of request r at plane
+ * `plane` reads position pos from plane min(plane, exit_depth) of the same
+ * layer, then attends exactly as decode does. Every such plane must hold
+ * the layer (ORC_ENOTHELD otherwise); a depth outside [0, num_planes) is
+ * ORC_EINVAL. */
+int orc_decode_latest(const orc_pool *pool, int32_t plane, int32_t layer,
+                      const int8_t *exit_depth, int32_t exit_stride,
+                      const void *q, int32_t num_q_heads,
+                      const int32_t *page_table, int32_t pt_stride,
+                      const int32_t *seq_lens, int32_t batch, double scale,
+                      double *out, double *lse);
+
 /* Split-K partials of decode: partition j covers positions
  * [j*partition, min((j+1)*partition, seq_len)). Per (request, q head, j):
  * m = max score, l = sum exp(s - m), acc = sum exp(s - m) * v.

@@ -48,6 +48,10 @@ MUTANTS = {
     "partition_bound": ("int32_t lo = j * partition;", "int32_t lo = j * partition + (j > 0);"),
     "prefill_position": ("int32_t pos = n - qlen + j;", "int32_t pos = j;"),
     "no_dup_check": ("if (sorted[i] == sorted[i - 1])", "if (0)"),
+    "latest_deepest": ("bank = bank_for(p, e < plane ? e : plane, layer);",
+                       "bank = bank_for(p, e > plane ? e : plane, layer);"),
+    "latest_ignored": ("bank = bank_for(p, e < plane ? e : plane, layer);",
+                       "bank = bank_for(p, plane, layer);"),
 }
 
 
@@ -122,6 +126,37 @@ def battery(lib) -> list[str]:
         ok = False
     if not ok:
         failed.append("prefill")
+
+    # early-exit decode vs brute force on a context picked plane by plane
+    try:
+        planes = 3
+        order = [(p, 1) for p in range(planes)]
+        case = synth.make_decode_case(5, "bf16", 3, (10, 40), 2, 2, 8, page_size=4,
+                                      num_planes=planes, num_layers=2, rec_first=1,
+                                      planes_layers=order)
+        pool = _pool(lib, case.layout)
+        for pl in order:
+            bd = case.banks[pl]
+            oracle.kv_write(pool, *pl, bd.fill_k, bd.fill_v, bd.fill_slots, lib=lib)
+            oracle.kv_write(pool, *pl, bd.new_k, bd.new_v, bd.new_slots, lib=lib)
+        depth = np.random.default_rng(1).integers(0, planes, size=(3, 40)).astype(np.int8)
+        ok = True
+        for p in range(planes):
+            q = case.banks[(p, 1)].q
+            o, l = oracle.decode_latest(pool, p, 1, depth, q, case.page_table, case.seq_lens,
+                                        lib=lib)
+            for r in range(case.batch):
+                n = int(case.seq_lens[r])
+                src = np.minimum(depth[r, :n], p)
+                lk = np.stack([case.banks[(int(src[t]), 1)].logical_k[r][t] for t in range(n)])
+                lv = np.stack([case.banks[(int(src[t]), 1)].logical_v[r][t] for t in range(n)])
+                bo_, bl_ = brute.attention(q[r:r + 1], lk, lv, np.array([n - 1]),
+                                           1 / math.sqrt(8))
+                ok = ok and _close(o[r], bo_[0]) and _close(l[r], bl_[0])
+    except oracle.OracleError:
+        ok = False
+    if not ok:
+        failed.append("decode_latest")
 
     # store_kv rejects a duplicate slot
     layout = synth.Layout("f32", 4, 3, 1, 4)
