@@ -129,9 +129,26 @@ class DecodeWorkload:
             hb = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
             self.snap.append((hb(k[b])[None], hb(v[b])[None], hb(self.q[i])))
 
+    def use_exit_depths(self, lo, hi, seed=7):
+        """Early exit: every context token halted at a depth drawn uniformly
+        from [lo, hi]; recurrent-layer calls then read each token from plane
+        min(plane, depth) (paged_decode_latest_attn)."""
+        import torch
+
+        rng = np.random.default_rng(seed)
+        stride = (self.max_seq + 15) // 16 * 16
+        depth = rng.integers(lo, hi + 1, size=(self.batch, stride)).astype(np.int8)
+        self.exit_depth = torch.from_numpy(depth).cuda()
+
     def call(self, i, decode_only=False):
         plane, layer = self.order[i]
         pkv = self.pkv
+        if getattr(self, "exit_depth", None) is not None and plane > 0:
+            pkv.decode_latest(self.pool, plane, layer, self.exit_depth, self.q[i], self.table_d,
+                              self.seq_d, self.max_seq, partition=self.partition, out=self.out,
+                              lse=self.lse, workspace=self.ws, k_new=self.nk[i],
+                              v_new=self.nv[i])
+            return
         if self.separate_write:
             if not decode_only:
                 pkv.kv_write(self.pool, plane, layer, self.nk[i], self.nv[i], self.slots)
@@ -349,6 +366,39 @@ def run_lotus(prompts=8, prompt_len=512, block=64, loop_iters=4, heads=32, D=128
                   "extend-prefill of the block)"}
     log(f"lotus: {res}")
     return res
+
+
+def run_latest_bank(steps=10, warmup=2):
+    """A Huginn-shaped decode step (132 bank calls) where context tokens
+    halted early at depths uniform in [20, 31] and recurrent-layer calls read
+    each token from its latest bank, next to the same step without early
+    exit. Logical KV bytes are the same in both."""
+    import torch
+
+    wl = make_workload("huginn", 0)
+    out = {}
+    for mode in ("all_planes", "latest_bank"):
+        if mode == "latest_bank":
+            wl.use_exit_depths(20, 31)
+        for _ in range(warmup):
+            wl.step()
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            wl.step()
+        e.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(e) / steps
+        out[mode] = {"ms_per_step": round(ms, 4),
+                     "kv_GBps": round(wl.kv_bytes_per_call * len(wl.order) / (ms / 1e3) / 1e9,
+                                      2)}
+    out["exit_depths"] = "uniform[20,31] per context token"
+    out["how"] = "paged_decode_latest_attn for plane >= 1 (store_kv of the newest token fused)"
+    log(f"latest bank: {out}")
+    del wl
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_page_mgr(reps=200):
@@ -585,6 +635,7 @@ def main():
         torch.cuda.empty_cache()
         res["prefill"] = run_prefill(supplementary=not args.no_supplementary)
         res["lotus"] = run_lotus()
+        res["latest_bank"] = run_latest_bank()
     res["page_manager"] = run_page_mgr()
     print(json.dumps(res), flush=True)
 

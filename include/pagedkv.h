@@ -186,6 +186,30 @@ int paged_decode_append_attn(const pkv_pool *pool, int32_t plane_id, int32_t lay
                              int32_t partition, void *out, float *lse,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* Decode with early exit: the "latest bank" ([FFM] "Can we actually stop
+ * early?": when the recurrent state converges, a token that halted at depth
+ * e keeps its depth-e KV, and later tokens attend that latest bank).
+ * exit_depth is DEVICE int8 [batch][exit_stride]: exit_depth[r][pos] is the
+ * deepest plane position pos of request r holds. The query of request r at
+ * plane_id reads position pos of layer layer_id from plane
+ * min(plane_id, exit_depth[r][pos]) -- the same page and slot in that
+ * plane's bank -- and otherwise this is paged_decode_attn (k_new, v_new
+ * NULL) or paged_decode_append_attn (k_new, v_new given; the newest token is
+ * written to and read from plane_id's bank). Requirements (checked, nothing
+ * enqueued otherwise): exit_depth 16-byte aligned; exit_stride a multiple of
+ * 16 and >= max_seq_len; every plane 0..plane_id holds layer_id
+ * (PKV_ENOTHELD), with the banks of planes 1..plane_id evenly spaced (true of
+ * every pkv_bank_map layout; PKV_EUNSUPPORTED otherwise); GQA group 1 or 2
+ * (PKV_EUNSUPPORTED otherwise). Device depths are not validated: a depth
+ * at or past plane_id (or negative) reads plane_id's own bank. */
+int paged_decode_latest_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                             const int8_t *exit_depth, int32_t exit_stride, const void *k_new,
+                             const void *v_new, const void *q, int32_t num_q_heads,
+                             const int32_t *page_table, int32_t page_table_stride,
+                             const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                             float scale, int32_t partition, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /* One decode step of a looped model: the decode calls of every (plane,
  * layer) the step visits, in the given order, enqueued by one host call
  * ([FFM] "Recurrent depth": loop iteration t of layer l is one attention

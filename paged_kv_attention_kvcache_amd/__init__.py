@@ -51,7 +51,8 @@ class _Pool(ctypes.Structure):
 
 
 EXPORTS = ("pkv_bank_map", "pkv_pool_bytes", "paged_kv_write", "paged_decode_workspace_bytes",
-           "paged_decode_attn", "paged_decode_append_attn", "paged_decode_split_mode",
+           "paged_decode_attn", "paged_decode_append_attn", "paged_decode_latest_attn",
+           "paged_decode_split_mode",
            "paged_decode_step", "paged_decode_step_capture", "paged_decode_step_graph_launch",
            "paged_decode_step_graph_destroy", "paged_decode_reduce", "paged_prefill_attn",
            "paged_extend_attn", "pkv_mgr_create", "pkv_mgr_destroy", "pkv_mgr_free_count",
@@ -81,6 +82,9 @@ def lib():
         L.paged_decode_append_attn.argtypes = [P, i32, i32, P, P, P, i32, P, i32, P, i32, i32,
                                                ctypes.c_float, i32, P, P, P, sz, P]
         L.paged_decode_append_attn.restype = ctypes.c_int
+        L.paged_decode_latest_attn.argtypes = [P, i32, i32, P, i32, P, P, P, i32, P, i32, P, i32,
+                                               i32, ctypes.c_float, i32, P, P, P, sz, P]
+        L.paged_decode_latest_attn.restype = ctypes.c_int
         L.paged_decode_split_mode.argtypes = [P, i32, i32, i32, i32]
         L.paged_decode_split_mode.restype = ctypes.c_int
         step = [P, i32, P, P, P, P, P, i32, P, i32, P, i32, i32, ctypes.c_float, i32, P, P, P,
@@ -248,6 +252,33 @@ def decode(pool: Pool, plane: int, layer: int, q, page_table, seq_lens, max_seq_
                                    int(page_table.shape[1]), _dptr(seq_lens), B, max_seq_len,
                                    float(scale), partition, _dptr(out), _dptr(lse),
                                    _dptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def decode_latest(pool: Pool, plane: int, layer: int, exit_depth, q, page_table, seq_lens,
+                  max_seq_len: int, scale: float | None = None, partition: int = 0, out=None,
+                  lse=None, workspace=None, with_lse: bool = True, stream=None, k_new=None,
+                  v_new=None):
+    """Early-exit decode (paged_decode_latest_attn): exit_depth int8 [B, stride]
+    (stride a multiple of 16, >= max_seq_len) gives each position's deepest
+    plane; position pos is read from plane min(plane, exit_depth[r, pos])."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(pool, B, Hq, max_seq_len, partition)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().paged_decode_latest_attn(
+        pool.ref, plane, layer, _dptr(exit_depth), int(exit_depth.shape[1]), _dptr(k_new),
+        _dptr(v_new), _dptr(q), Hq, _dptr(page_table), int(page_table.shape[1]),
+        _dptr(seq_lens), B, max_seq_len, float(scale), partition, _dptr(out), _dptr(lse),
+        _dptr(workspace), ws_bytes, _stream(stream)))
     return out, lse
 
 

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(64 * W) void decode_block(
     int32_t max_parts, typename E::storage *__restrict__ out, float *__restrict__ lse,
     float *__restrict__ part_m, float *__restrict__ part_l, float *__restrict__ part_acc,
     const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
-    uint4 *kb_w, uint4 *vb_w) {
+    uint4 *kb_w, uint4 *vb_w, LatestArgs la) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   constexpr int kThreads = 64 * W;
   __shared__ float2 lds_ml[W * G];
@@ -79,6 +79,7 @@ __global__ __launch_bounds__(64 * W) void decode_block(
   const int hi = min(lo + partition, n);
 
   F f(q + ((size_t)r * hq + (size_t)kvh * G) * D, qscale);
+  if constexpr (F::kLatest) f.la = la;
   typename F::State st;
   f.reset(st);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -93,7 +94,8 @@ __global__ __launch_bounds__(64 * W) void decode_block(
                    n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
   }
   if (npw > 0)
-    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p_first + w, npw, W, lo, hi);
+    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p_first + w, npw, W, lo, hi,
+                 F::kLatest ? la.depth + (size_t)r * la.stride : nullptr);
   f.finish_wave(st);
   emit_to_lds(f, st, w, lds_ml, lds_acc);
   __syncthreads();
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(64 * W) void decode_whole(
     const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
     typename E::storage *__restrict__ out, float *__restrict__ lse,
     const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
-    uint4 *kb_w, uint4 *vb_w) {
+    uint4 *kb_w, uint4 *vb_w, LatestArgs la) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   constexpr int kThreads = 64 * W;
   __shared__ float2 lds_ml[W * G];
@@ -166,6 +168,7 @@ __global__ __launch_bounds__(64 * W) void decode_whole(
     const int n = __builtin_amdgcn_readlane(mine, r);
 
     F f(q + ((size_t)r * hq + (size_t)kvh * G) * D, qscale);
+    if constexpr (F::kLatest) f.la = la;
     typename F::State st;
     f.reset(st);
     const int n_pages = (n + kPage - 1) / kPage;
@@ -177,7 +180,9 @@ __global__ __launch_bounds__(64 * W) void decode_whole(
         f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
                      n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
     }
-    if (npw > 0) stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, w, npw, W, 0, n);
+    if (npw > 0)
+      stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, w, npw, W, 0, n,
+                   F::kLatest ? la.depth + (size_t)r * la.stride : nullptr);
     f.finish_wave(st);
     emit_to_lds(f, st, w, lds_ml, lds_acc);
     __syncthreads();
@@ -211,9 +216,9 @@ __global__ __launch_bounds__(128) void decode_reduce(
   }
 }
 
-template <typename E, int D, int G>
-static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
-  using F = typename FoldFor<E, D, G>::type;
+template <typename E, class F>
+static hipError_t decode_fold(const DecodeArgs &a, hipStream_t stream) {
+  constexpr int D = F::kHeadDim;
   const dim3 grid(a.max_parts, a.bank.num_kv_heads, a.batch);
   constexpr int W = decode_waves<F>();
   if (a.max_parts == 1 && a.batch <= kWholeMaxBatch) {
@@ -237,7 +242,8 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
                        a.scale * kLog2e, static_cast<typename E::storage *>(a.out), a.lse,
                        static_cast<const typename E::storage *>(a.k_new),
                        static_cast<const typename E::storage *>(a.v_new),
-                       static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
+                       static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v),
+                       a.latest);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((decode_block<E, F, W>), grid, dim3(64 * W), 0, stream,
@@ -248,7 +254,7 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
                      a.max_parts, static_cast<typename E::storage *>(a.out), a.lse, a.part_m,
                      a.part_l, a.part_acc, static_cast<const typename E::storage *>(a.k_new),
                      static_cast<const typename E::storage *>(a.v_new),
-                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
+                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v), a.latest);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, D, a.seq_lens, a.max_seq_len,
@@ -258,11 +264,18 @@ static hipError_t decode_valu(const DecodeArgs &a, hipStream_t stream) {
 
 template <typename E, int D>
 static hipError_t decode_by_group(const DecodeArgs &a, hipStream_t stream) {
+  if (a.latest.depth) {  // early exit: vector folds of groups 1 and 2
+    switch (a.num_q_heads / a.bank.num_kv_heads) {
+      case 1: return decode_fold<E, ValuFold<E, D, 1, true>>(a, stream);
+      case 2: return decode_fold<E, ValuFold<E, D, 2, true>>(a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.num_q_heads / a.bank.num_kv_heads) {
-    case 1: return decode_valu<E, D, 1>(a, stream);
-    case 2: return decode_valu<E, D, 2>(a, stream);
-    case 4: return decode_valu<E, D, 4>(a, stream);
-    case 8: return decode_valu<E, D, 8>(a, stream);
+    case 1: return decode_fold<E, typename FoldFor<E, D, 1>::type>(a, stream);
+    case 2: return decode_fold<E, typename FoldFor<E, D, 2>::type>(a, stream);
+    case 4: return decode_fold<E, typename FoldFor<E, D, 4>::type>(a, stream);
+    case 8: return decode_fold<E, typename FoldFor<E, D, 8>::type>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kBlock) void decode_stream(
     typename E::storage *__restrict__ out, float *__restrict__ lse,
     float2 *__restrict__ part_ml, float *__restrict__ part_acc,
     const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
-    uint4 *kb_w, uint4 *vb_w) {
+    uint4 *kb_w, uint4 *vb_w, LatestArgs la) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   extern __shared__ int cum[];  // [batch + 1]
   row_prefix(seq_lens, batch, max_seq_len, hkv, cum);
@@ -103,6 +103,7 @@ __global__ __launch_bounds__(kBlock) void decode_stream(
     const int n = min(max(seq_lens[r], 0), max_seq_len);
     const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
     F f(q + row0 * D, qscale);
+    if constexpr (F::kLatest) f.la = la;
     typename F::State st;
     f.reset(st);
     const int32_t *pt_row = page_table + (size_t)r * pt_stride;
@@ -112,7 +113,8 @@ __global__ __launch_bounds__(kBlock) void decode_stream(
         f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
                      n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
     }
-    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p, len, 1, 0, n);
+    stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p, len, 1, 0, n,
+                 F::kLatest ? la.depth + (size_t)r * la.stride : nullptr);
     f.finish_wave(st);
     if (p == 0 && len == pr) {  // the whole unit: finish here
       emit_final<F, E>(f, st, out, lse, row0);
@@ -280,11 +282,11 @@ int stream_waves(int dtype, int head_dim, int group, int num_cus) {
   return num_cus * bpc * kWaves;
 }
 
-template <typename E, int D, int G>
+template <typename E, int D, int G, class F = typename FoldFor<E, D, G>::type>
 static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t stream) {
   const unsigned blocks = (unsigned)(nw / kWaves);
   const size_t lds = sizeof(int) * ((size_t)a.batch + 1);
-  hipLaunchKernelGGL((decode_stream<E, typename FoldFor<E, D, G>::type>), dim3(blocks), dim3(kBlock), lds, stream,
+  hipLaunchKernelGGL((decode_stream<E, F>), dim3(blocks), dim3(kBlock), lds, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads,
                      static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
@@ -293,7 +295,7 @@ static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t str
                      reinterpret_cast<float2 *>(a.part_m), a.part_acc,
                      static_cast<const typename E::storage *>(a.k_new),
                      static_cast<const typename E::storage *>(a.v_new),
-                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v));
+                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v), a.latest);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_stream_combine<E, G>), dim3(a.batch * a.bank.num_kv_heads),
@@ -305,6 +307,13 @@ static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t str
 
 template <typename E, int D>
 static hipError_t stream_by_group(const DecodeArgs &a, int64_t nw, hipStream_t stream) {
+  if (a.latest.depth) {  // early exit: vector folds of groups 1 and 2
+    switch (a.num_q_heads / a.bank.num_kv_heads) {
+      case 1: return stream_launch<E, D, 1, ValuFold<E, D, 1, true>>(a, nw, stream);
+      case 2: return stream_launch<E, D, 2, ValuFold<E, D, 2, true>>(a, nw, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.num_q_heads / a.bank.num_kv_heads) {
     case 1: return stream_launch<E, D, 1>(a, nw, stream);
     case 2: return stream_launch<E, D, 2>(a, nw, stream);

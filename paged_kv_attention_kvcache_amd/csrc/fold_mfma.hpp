@@ -28,6 +28,7 @@ template <int G>
 struct MfmaFold {
   static_assert(G == 4 || G == 8, "MFMA fold covers GQA groups of 4 and 8");
   static constexpr int kPagesPerStep = 2;
+  static constexpr bool kLatest = false;
   static constexpr int kDepth = 2;  // steps in flight per wave
   static constexpr int kGroup = G;
   static constexpr int kHeadDim = 128;

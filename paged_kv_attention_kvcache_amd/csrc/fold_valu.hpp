@@ -27,9 +27,11 @@ template <typename E, int D> struct Tile {
   static_assert(kLPT == 8 || kLPT == 16 || kLPT == 32, "unsupported head_dim");
 };
 
-template <typename E, int D, int G>
+// L: early-exit decode, each token row loaded from its own plane's bank.
+template <typename E, int D, int G, bool L = false>
 struct ValuFold {
   using TL = Tile<E, D>;
+  static constexpr bool kLatest = L;
   static constexpr int N = TL::kVecN, LPT = TL::kLPT, RPW = TL::kRPW, NI = TL::kNI;
   static constexpr int kPagesPerStep = 1;
   static constexpr int kDepth = 2;  // steps in flight per wave (3 measured slower)
@@ -51,6 +53,7 @@ struct ValuFold {
   // in that page (-1: none) and this lane's 16-byte chunk of its K and V rows.
   int app_page = -1, app_tok = -1;
   uint4 app_k, app_v;
+  LatestArgs la{};  // early-exit decode (L only)
 
   // qrow: the first of the G query rows (contiguous, head_dim each).
   __device__ __forceinline__ ValuFold(const typename E::storage *__restrict__ qrow, float qs)
@@ -105,6 +108,29 @@ struct ValuFold {
     for (int i = 0; i < NI; ++i) r.k[i] = load_stream(kt + lane_off + i * RPW * LPT * 16u);
 #pragma unroll
     for (int i = 0; i < NI; ++i) r.v[i] = load_stream(vt + lane_off + i * RPW * LPT * 16u);
+  }
+
+  // Early-exit variant of load: `ex` holds the 16 exit depths of the page's
+  // tokens (byte t = token t). The row of token t is read from the bank of
+  // plane min(la.plane, depth); bytes past the plane (and ones that would be
+  // negative as int8) read the query's own plane, so every address stays in
+  // a bank the call was validated for.
+  __device__ __forceinline__ void load_latest(Regs &r, const uint4 *__restrict__ kb,
+                                              const uint4 *__restrict__ vb, int page,
+                                              const uint4 &ex, int hkv, int kvh) const {
+    const size_t tile = ((size_t)page * hkv + kvh) * TL::kTileVec;
+    const char *kt = reinterpret_cast<const char *>(kb + tile);
+    const char *vt = reinterpret_cast<const char *>(vb + tile);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = row + i * RPW;  // token of load i within the page
+      const uint32_t w = (t >> 2) == 0 ? ex.x : (t >> 2) == 1 ? ex.y : (t >> 2) == 2 ? ex.z : ex.w;
+      const int e = min((int)((w >> (8 * (t & 3))) & 0xffu), la.plane);
+      const int64_t delta = e == 0 ? la.d0 : la.d1 + (int64_t)(e - 1) * la.step;
+      const uint32_t off = lane_off + i * RPW * LPT * 16u;
+      r.k[i] = load_stream(kt + delta + off);
+      r.v[i] = load_stream(vt + delta + off);
+    }
   }
 
   // Folds page pi of the request (keys outside [lo, hi) masked). The page

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace pkv {
 
 // Sets the thread's last-error message (pkv_last_error) and returns code.
@@ -44,6 +46,7 @@ struct DecodeArgs {
   // the same kernel. NULL: the pool already holds it.
   const void *k_new = nullptr, *v_new = nullptr;
   int32_t num_cus = 256;  // compute units of the device (sizes persistent grids)
+  LatestArgs latest{};    // early-exit decode when latest.depth != null
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -209,7 +209,8 @@ int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const 
                 const void *v_new, const void *q, int32_t num_q_heads,
                 const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
                 int32_t batch, int32_t max_seq_len, float scale, int32_t partition, void *out,
-                float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+                float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                const pkv::LatestArgs *latest = nullptr) {
   pkv::Bank bank;
   int rc = resolve_bank(pool, plane_id, layer_id, &bank);
   if (rc) return rc;
@@ -252,6 +253,7 @@ int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const 
   a.k_new = k_new;
   a.v_new = v_new;
   a.num_cus = device_cus();
+  if (latest) a.latest = *latest;
   char *ws = static_cast<char *>(workspace);
   if (stream_mode) {
     const int64_t nw = stream_wave_count(pool, batch, num_q_heads, max_seq_len);
@@ -384,6 +386,53 @@ void paged_decode_step_graph_destroy(pkv_step_graph *graph) {
   (void)hipGraphExecDestroy(graph->exec);
   (void)hipGraphDestroy(graph->graph);
   delete graph;
+}
+
+int paged_decode_latest_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                             const int8_t *exit_depth, int32_t exit_stride, const void *k_new,
+                             const void *v_new, const void *q, int32_t num_q_heads,
+                             const int32_t *page_table, int32_t page_table_stride,
+                             const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+                             float scale, int32_t partition, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  pkv::Bank bank;
+  int rc = resolve_bank(pool, plane_id, layer_id, &bank);
+  if (rc) return rc;
+  if (!exit_depth) return fail(PKV_EINVAL, "exit_depth is NULL");
+  if (reinterpret_cast<uintptr_t>(exit_depth) & 15)
+    return fail(PKV_EINVAL, "exit_depth must be 16-byte aligned");
+  if (exit_stride <= 0 || exit_stride % 16 != 0 || exit_stride < (max_seq_len + 15) / 16 * 16)
+    return fail(PKV_EINVAL, "exit_stride %d must be a multiple of 16 covering max_seq_len %d",
+                exit_stride, max_seq_len);
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0 ||
+      (num_q_heads / pool->num_kv_heads != 1 && num_q_heads / pool->num_kv_heads != 2))
+    return fail(PKV_EUNSUPPORTED, "early-exit decode supports GQA groups of 1 and 2");
+  if (!k_new != !v_new) return fail(PKV_EINVAL, "k_new and v_new must both be given or both NULL");
+  if (k_new && ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15))
+    return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  // Every plane up to the query's must hold the layer; the banks of planes
+  // 1..plane_id must be evenly spaced (true of every per-plane map).
+  const int32_t *row = pool->bank_of;
+  auto bank_at = [&](int32_t p) { return row[(size_t)p * pool->num_layers + layer_id]; };
+  for (int32_t p = 0; p <= plane_id; ++p)
+    if (bank_at(p) < 0 || bank_at(p) >= pool->num_banks)
+      return fail(PKV_ENOTHELD, "plane %d does not hold layer %d", p, layer_id);
+  for (int32_t p = 3; p <= plane_id; ++p)
+    if (bank_at(p) - bank_at(p - 1) != bank_at(2) - bank_at(1))
+      return fail(PKV_EUNSUPPORTED, "banks of layer %d are not evenly spaced over planes 1..%d",
+                  layer_id, plane_id);
+  const int64_t bank_bytes = (int64_t)pool->num_pages * pool->num_kv_heads * pool->page_size *
+                             pool->head_dim * elem_bytes(pool->dtype);
+  pkv::LatestArgs la{};
+  la.depth = reinterpret_cast<const uint8_t *>(exit_depth);
+  la.stride = exit_stride;
+  la.plane = plane_id;
+  la.d0 = (int64_t)(bank_at(0) - bank_at(plane_id)) * bank_bytes;
+  la.d1 = plane_id >= 1 ? (int64_t)(bank_at(1) - bank_at(plane_id)) * bank_bytes : 0;
+  la.step = plane_id >= 2 ? (int64_t)(bank_at(2) - bank_at(1)) * bank_bytes : 0;
+  return decode_impl(pool, plane_id, layer_id, k_new, v_new, q, num_q_heads, page_table,
+                     page_table_stride, seq_lens, batch, max_seq_len, scale, partition, out, lse,
+                     workspace, workspace_bytes, stream, &la);
 }
 
 int paged_decode_split_mode(const pkv_pool *pool, int32_t batch, int32_t num_q_heads,

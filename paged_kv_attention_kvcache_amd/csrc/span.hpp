@@ -28,13 +28,19 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
                                              const uint4 *__restrict__ vb,
                                              const int32_t *__restrict__ pt_row,
                                              int32_t num_pages, int32_t hkv, int32_t kvh,
-                                             int p_first, int count, int stride, int lo, int hi) {
+                                             int p_first, int count, int stride, int lo, int hi,
+                                             const uint8_t *__restrict__ ex_row = nullptr) {
   constexpr int S = F::kPagesPerStep;
   const int lane = threadIdx.x & 63;
   for (int base = 0; base < count; base += 64) {
     const int cnt = min(64, count - base);
     int pid = 0;
-    if (lane < cnt) pid = min(max(pt_row[p_first + stride * (base + lane)], 0), num_pages - 1);
+    uint4 ex = make_uint4(0u, 0u, 0u, 0u);  // early exit: the page's 16 exit depths
+    if (lane < cnt) {
+      const int pi = p_first + stride * (base + lane);
+      pid = min(max(pt_row[pi], 0), num_pages - 1);
+      if constexpr (F::kLatest) ex = *reinterpret_cast<const uint4 *>(ex_row + 16 * (size_t)pi);
+    }
     const int pi0 = p_first + stride * base;  // page index of k = 0
     const int steps = (cnt + S - 1) / S;
     // Page id and page index of the k-th page of this chunk; a page past the
@@ -42,7 +48,16 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
     auto page = [&](int k) { return __builtin_amdgcn_readlane(pid, min(k, cnt - 1)); };
     auto index = [&](int k) { return k < cnt ? pi0 + stride * k : -1; };
     auto load = [&](typename F::Regs &r, int s) {
-      f.load(r, kb, vb, page(s * S), page(s * S + S - 1), hkv, kvh);
+      if constexpr (F::kLatest) {
+        const int k = min(s, cnt - 1);  // one page per step
+        const uint4 e = make_uint4(__builtin_amdgcn_readlane(ex.x, k),
+                                   __builtin_amdgcn_readlane(ex.y, k),
+                                   __builtin_amdgcn_readlane(ex.z, k),
+                                   __builtin_amdgcn_readlane(ex.w, k));
+        f.load_latest(r, kb, vb, page(s), e, hkv, kvh);
+      } else {
+        f.load(r, kb, vb, page(s * S), page(s * S + S - 1), hkv, kvh);
+      }
     };
     // A fold ends with a compiler-only barrier: the next load into the same
     // registers must not be hoisted above it (that needs a second register

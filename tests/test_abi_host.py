@@ -193,3 +193,17 @@ def test_decode_step_validation(L):
     assert not handle.value
     assert L.paged_decode_step_graph_launch(None, None) == pkv.PKV_EINVAL
     L.paged_decode_step_graph_destroy(None)  # a no-op
+
+
+def test_decode_latest_validation(L):
+    st, keep = _pool(planes=4, layers=3, rec=(1, 2), kv=2)
+    call = lambda plane=2, layer=1, ed=FAKE, stride=64, hq=2, **o: L.paged_decode_latest_attn(
+        ctypes.byref(st), plane, layer, ed, stride, None, None, FAKE, hq, FAKE, 4, FAKE, 2,
+        o.get("max_seq", 64), 1.0, 0, FAKE, None, FAKE, 1 << 30, None)
+    assert call(ed=None) == pkv.PKV_EINVAL
+    assert call(ed=FAKE + 8) == pkv.PKV_EINVAL          # not 16-byte aligned
+    assert call(stride=40) == pkv.PKV_EINVAL            # not a multiple of 16
+    assert call(stride=48) == pkv.PKV_EINVAL            # shorter than max_seq_len
+    assert call(hq=8) == pkv.PKV_EUNSUPPORTED           # group 4
+    assert call(layer=0, plane=1) == pkv.PKV_ENOTHELD   # plane 1 does not hold layer 0
+    assert call(layer=0, plane=0, max_seq=65) == pkv.PKV_EINVAL  # beyond stride * page_size
