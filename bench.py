@@ -112,7 +112,7 @@ class DecodeWorkload:
         g = hq // hkv
         fold = f"MfmaFold<{g}>" if g in (4, 8) and D == 128 else f"ValuFold<BF16, {D}, {g}>"
         self.kernel_name = {
-            "whole": f"decode_whole<BF16, {fold}> (one launch per call)",
+            "whole": f"decode_whole<BF16, {fold}> (persistent, one launch per call)",
             "balanced": f"decode_stream<BF16, {fold}> + decode_stream_combine",
             "fixed": f"decode_block<BF16, {fold}> + decode_reduce"}[self.split]
         # algorithmic bytes: each request reads its whole context (K and V)
