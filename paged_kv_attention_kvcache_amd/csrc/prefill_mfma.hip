@@ -6,9 +6,10 @@
 // attend); packed query row j of request r sits at position seq_len - q_len
 // + j and sees keys 0..that position.
 //
-// Work: one workgroup per (tile of 128 query rows, q head, request), launched
-// heaviest tiles (latest rows, most keys) first; wave w owns rows 32w..32w+31
-// of the tile as two blocks of 16 query columns. The contraction runs on
+// Work: the tiles of 128 query rows of a (request, q head) see 1..T steps of
+// keys, so one workgroup folds the pair of tiles T-1-p and p, one after the
+// other, and every workgroup carries about the same number of keys; wave w
+// owns rows 32w..32w+31 of a tile as two blocks of 16 query columns. The contraction runs on
 // v_mfma_f32_16x16x32_bf16 in the transposed form
 //   S^T = K Q^T   (A = 16 keys x 32 dims from a row-major K tile),
 //   O^T += V^T P^T (A = 16 dims x 32 keys, B = 32 keys x 16 queries),
@@ -55,6 +56,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kTileRows = 128;    // query rows per workgroup
+constexpr int kXcds = 8;          // accelerator dies; workgroups are dealt to them round-robin
 constexpr int kTileBytes = 4096;  // one (page, kv head) tile
 constexpr float kLazy = 8.f;      // rescale threshold (log2 units)
 
@@ -145,22 +147,34 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   __shared__ __attribute__((aligned(1024))) uint4 ring[RING * kStageBytes / 16];
   __shared__ int32_t pids[MAXP];
 
-  // Heaviest tiles first; within a tile index, the q heads of one request are
-  // adjacent (the heads of a GQA group read the same K/V).
-  const int per_t = hq * batch;
+  // Causal tiles see 1, 2, ..., T steps of keys, so they are paired: the
+  // workgroup of pair p folds tile T-1-p and then tile p of its (request,
+  // head), and every pair carries about the same number of keys.
+  //
+  // Workgroup i runs on XCD i % 8 (round-robin dispatch), and each XCD has
+  // its own L2. The pairs of one (request, head) are given ids on the same
+  // XCD and next to each other in its dispatch order (id / 8), so they run
+  // at the same time, stream the same K/V steps from key 0 up at about the
+  // same pace, and read them through one L2. Each XCD takes a contiguous
+  // block of (request, head) units, so the q heads of a GQA group (which
+  // read the same K/V) share an L2 too.
+  const int npairs = (tiles + 1) / 2;
+  const int per_xcd = (hq * batch + kXcds - 1) / kXcds;
   const int id = (int)blockIdx.x;
-  const int t = tiles - 1 - id / per_t;
-  const int h = (id % per_t) % hq, r = (id % per_t) / hq;
+  const int slot = id / kXcds;
+  const int pr = slot % npairs;
+  const int unit = (id % kXcds) * per_xcd + slot / npairs;  // (request, head) = (r, h)
+  if (slot / npairs >= per_xcd || unit >= hq * batch) return;
+  const int h = unit % hq, r = unit / hq;
   const int kvh = h / (hq / hkv);
   const int q0 = cu_q_lens[r];
   const int n = min(max(seq_lens[r], 0), max_seq_len);
   const int q_len = min(max(cu_q_lens[r + 1] - q0, 0), n);
-  if (t * kTileRows >= q_len) return;
+  const int tiles_r = (q_len + kTileRows - 1) / kTileRows;
+  if (pr >= (tiles_r + 1) / 2) return;
   const int p0 = n - q_len;  // position of query row 0
-  const int row_lo = t * kTileRows, row_hi = min(row_lo + kTileRows, q_len);
-  const int key_end = p0 + row_hi;  // keys [0, key_end) are visible to the tile
-  const int steps = (key_end + kStepKeys - 1) / kStepKeys;
-  const int kpages = min((key_end + kPage - 1) / kPage, MAXP);
+  const int t_hi = tiles_r - 1 - pr;  // the pair's later tile
+  const int kpages = min((p0 + min((t_hi + 1) * kTileRows, q_len) + kPage - 1) / kPage, MAXP);
   const int32_t *pt_row = page_table + (size_t)r * pt_stride;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -198,33 +212,6 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
     }
   };
 
-  // Q operands (B of S^T): block b, query row wrow0 + 16b + nl, chunk 4c + g4.
-  // A negative scale moves into Q's sign bits (exact), so the scale applied
-  // to scores is positive; a zero scale becomes the smallest normal float
-  // (scores of at most ~1e4 then give exp2 of exactly 1).
-  float qs = qscale;
-  uint32_t sgn = 0;
-  if (qs < 0.f) {
-    qs = -qs;
-    sgn = 0x80008000u;
-  }
-  if (!(qs > 0.f)) qs = FLT_MIN;
-  const int wrow0 = row_lo + w * 32;
-  uint4 qb[2][4];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int row = wrow0 + 16 * b + nl;
-    const bool ok = row < row_hi;
-    const uint4 *qr =
-        reinterpret_cast<const uint4 *>(q + ((size_t)(q0 + (ok ? row : 0)) * hq + h) * 128);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 x = qr[4 * c + g4];
-      qb[b][c] = ok ? make_uint4(x.x ^ sgn, x.y ^ sgn, x.z ^ sgn, x.w ^ sgn)
-                    : make_uint4(0, 0, 0, 0);
-    }
-  }
-
   // LDS read offsets within a tile. K: token nl, chunk 4c + g4. V (transposed
   // read for dims 16 sl .. +15): token 4 g4 + nl/4, dims 16 sl + 4 (nl%4) .. +3.
   const int gk = rot4(nl);
@@ -238,157 +225,192 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   for (int sl = 0; sl < 8; ++sl)
     voff[sl] = (uint32_t)(tv * 16 + ((2 * sl + ((nl >> 1) & 1)) ^ gv)) * 16u + (nl & 1) * 8u;
 
-  // acc[b][sl]: O^T tiles; l[b]: this lane's part of the softmax denominator
-  // (its keys), summed in fp32 before the probabilities are rounded to bf16.
-  f32x4 acc[2][8];
-  float m[2], l[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[b] = -INFINITY;
-    l[b] = 0.f;
+  // Q operands (B of S^T): block b, query row wrow0 + 16b + nl, chunk 4c + g4.
+  // A negative scale moves into Q's sign bits (exact), so the scale applied
+  // to scores is positive; a zero scale becomes the smallest normal float
+  // (scores of at most ~1e4 then give exp2 of exactly 1).
+  float qs = qscale;
+  uint32_t sgn = 0;
+  if (qs < 0.f) {
+    qs = -qs;
+    sgn = 0x80008000u;
   }
-  const int wave_rows = max(0, min(32, row_hi - wrow0));
-  const int wave_last = p0 + wrow0 + wave_rows - 1;  // last query position of the wave
-
-  static_for<RING - 1>([&](auto j) {
-    if (decltype(j)::value < steps) issue(decltype(j)::value, j);
-  });
-
-  const lds_char *ringb = (const lds_char *)ring;
-  // One step; the stage index is a compile-time constant (the loop below is
-  // unrolled by RING), so every LDS address is a per-lane base plus an
-  // immediate offset.
-  auto step = [&](int s, auto stage) {
-    // stages issued after this one, each kTPW * 4 copies per wave
-    wait_ahead<kTPW * 4, RING - 2>(min(RING - 2, steps - 1 - s));
-    if (s + RING - 1 < steps)
-      issue(s + RING - 1, std::integral_constant<int, (decltype(stage)::value + RING - 1) % RING>{});
-
-    const int k0 = s * kStepKeys;
-    const lds_char *st = ringb + decltype(stage)::value * kStageBytes;
-    const bool tail = k0 + kStepKeys > n;
-    if (tail) {
-      // Token rows at or beyond the context end may hold anything (NaN
-      // included) and meet probability 0 in the PV product: zero their V.
-      lds_u32x4 *vst = (lds_u32x4 *)(st + SP * kTileBytes);
+  if (!(qs > 0.f)) qs = FLT_MIN;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int t = pass == 0 ? t_hi : pr;
+    if (pass == 1 && t == t_hi) break;  // the middle tile of an odd count
+    if (pass == 1) __syncthreads();  // the second tile refills the ring
+    const int row_lo = t * kTileRows, row_hi = min(row_lo + kTileRows, q_len);
+    const int key_end = p0 + row_hi;  // keys [0, key_end) are visible to the tile
+    const int steps = (key_end + kStepKeys - 1) / kStepKeys;
+    const int wrow0 = row_lo + w * 32;
+    uint4 qb[2][4];
 #pragma unroll
-      for (int i = 0; i < SP; ++i) {
-        const int chunk = tid + kBlock * i;  // V tile i, token tid / 16
-        if (k0 + 16 * i + (tid >> 4) >= n) vst[chunk] = u32x4{0u, 0u, 0u, 0u};
+    for (int b = 0; b < 2; ++b) {
+      const int row = wrow0 + 16 * b + nl;
+      const bool ok = row < row_hi;
+      const uint4 *qr =
+          reinterpret_cast<const uint4 *>(q + ((size_t)(q0 + (ok ? row : 0)) * hq + h) * 128);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 x = qr[4 * c + g4];
+        qb[b][c] = ok ? make_uint4(x.x ^ sgn, x.y ^ sgn, x.z ^ sgn, x.w ^ sgn)
+                      : make_uint4(0, 0, 0, 0);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (wave_rows == 0 || k0 > wave_last) return;  // nothing visible to this wave
 
-    // S^T for the step's pages, both query blocks (K reads shared), two pages
-    // at a time with the dim chunk outermost: consecutive MFMAs update four
-    // different accumulators, so none waits on the one before.
-    f32x4 S[2][SP];
+    // acc[b][sl]: O^T tiles; l[b]: this lane's part of the softmax denominator
+    // (its keys), summed in fp32 before the probabilities are rounded to bf16.
+    f32x4 acc[2][8];
+    float m[2], l[2];
 #pragma unroll
-    for (int P2 = 0; P2 < SP; P2 += 2) {
-      uint4 kr[2][4];
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
+      for (int j = 0; j < 8; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[b] = -INFINITY;
+      l[b] = 0.f;
+    }
+    const int wave_rows = max(0, min(32, row_hi - wrow0));
+    const int wave_last = p0 + wrow0 + wave_rows - 1;  // last query position of the wave
+
+    static_for<RING - 1>([&](auto j) {
+      if (decltype(j)::value < steps) issue(decltype(j)::value, j);
+    });
+
+    const lds_char *ringb = (const lds_char *)ring;
+    // One step; the stage index is a compile-time constant (the loop below is
+    // unrolled by RING), so every LDS address is a per-lane base plus an
+    // immediate offset.
+    auto step = [&](int s, auto stage) {
+      // stages issued after this one, each kTPW * 4 copies per wave
+      wait_ahead<kTPW * 4, RING - 2>(min(RING - 2, steps - 1 - s));
+      if (s + RING - 1 < steps)
+        issue(s + RING - 1, std::integral_constant<int, (decltype(stage)::value + RING - 1) % RING>{});
+
+      const int k0 = s * kStepKeys;
+      const lds_char *st = ringb + decltype(stage)::value * kStageBytes;
+      const bool tail = k0 + kStepKeys > n;
+      if (tail) {
+        // Token rows at or beyond the context end may hold anything (NaN
+        // included) and meet probability 0 in the PV product: zero their V.
+        lds_u32x4 *vst = (lds_u32x4 *)(st + SP * kTileBytes);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          kr[pp][c] = __builtin_bit_cast(
-              uint4, *(const lds_u32x4 *)(st + (P2 + pp) * kTileBytes + koff[c]));
+        for (int i = 0; i < SP; ++i) {
+          const int chunk = tid + kBlock * i;  // V tile i, token tid / 16
+          if (k0 + 16 * i + (tid >> 4) >= n) vst[chunk] = u32x4{0u, 0u, 0u, 0u};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (wave_rows == 0 || k0 > wave_last) return;  // nothing visible to this wave
+
+      // S^T for the step's pages, both query blocks (K reads shared), two pages
+      // at a time with the dim chunk outermost: consecutive MFMAs update four
+      // different accumulators, so none waits on the one before.
+      f32x4 S[2][SP];
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int P2 = 0; P2 < SP; P2 += 2) {
+        uint4 kr[2][4];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
-            S[b][P2 + pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16(kr[pp][c]), as_bf16(qb[b][c]),
-                c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[b][P2 + pp], 0, 0, 0);
-    }
-    // Keys after a query or beyond the context are masked (only on steps
-    // that cross the diagonal or the end of the context).
-    if (tail || k0 + kStepKeys - 1 > p0 + wrow0) {
+          for (int c = 0; c < 4; ++c)
+            kr[pp][c] = __builtin_bit_cast(
+                uint4, *(const lds_u32x4 *)(st + (P2 + pp) * kTileBytes + koff[c]));
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+              S[b][P2 + pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  as_bf16(kr[pp][c]), as_bf16(qb[b][c]),
+                  c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[b][P2 + pp], 0, 0, 0);
+      }
+      // Keys after a query or beyond the context are masked (only on steps
+      // that cross the diagonal or the end of the context).
+      if (tail || k0 + kStepKeys - 1 > p0 + wrow0) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          // key k0 + 4 g4 + (16 P + i) is visible iff 16 P + i <= lim
+          const int lim = min(p0 + wrow0 + 16 * b + nl, n - 1) - k0 - 4 * g4;
+#pragma unroll
+          for (int P = 0; P < SP; ++P)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * P + i > lim) S[b][P][i] = -INFINITY;
+        }
+      }
+
+      uint4 pb[2][SP / 2];  // P^T operands [block][half step]: keys 4 g4 + i of pages 2hs, 2hs+1
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        // key k0 + 4 g4 + (16 P + i) is visible iff 16 P + i <= lim
-        const int lim = min(p0 + wrow0 + 16 * b + nl, n - 1) - k0 - 4 * g4;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4 * SP; e += 2) mx = max3(mx, S[b][e >> 2][e & 3], S[b][e >> 2][(e & 3) + 1]);
+        const float mxs = col_max(mx) * qs;
+        if (__any(mxs > m[b] + kLazy)) {
+          const float mn = fmaxf(m[b], mxs);
+          const float alpha = fast_exp2(m[b] - ((mn == -INFINITY) ? 0.f : mn));
+          l[b] *= alpha;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[b][j] *= alpha;
+          m[b] = mn;
+        }
+        const float nms = (m[b] == -INFINITY) ? 0.f : -m[b];
+        float p[SP][4], lsum = 0.f;
 #pragma unroll
         for (int P = 0; P < SP; ++P)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * P + i > lim) S[b][P][i] = -INFINITY;
-      }
-    }
-
-    uint4 pb[2][SP / 2];  // P^T operands [block][half step]: keys 4 g4 + i of pages 2hs, 2hs+1
+          for (int i = 0; i < 4; ++i) {
+            p[P][i] = fast_exp2(fmaf(S[b][P][i], qs, nms));
+            lsum += p[P][i];
+          }
+        l[b] += lsum;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4 * SP; e += 2) mx = max3(mx, S[b][e >> 2][e & 3], S[b][e >> 2][(e & 3) + 1]);
-      const float mxs = col_max(mx) * qs;
-      if (__any(mxs > m[b] + kLazy)) {
-        const float mn = fmaxf(m[b], mxs);
-        const float alpha = fast_exp2(m[b] - ((mn == -INFINITY) ? 0.f : mn));
-        l[b] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[b][j] *= alpha;
-        m[b] = mn;
-      }
-      const float nms = (m[b] == -INFINITY) ? 0.f : -m[b];
-      float p[SP][4], lsum = 0.f;
-#pragma unroll
-      for (int P = 0; P < SP; ++P)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[P][i] = fast_exp2(fmaf(S[b][P][i], qs, nms));
-          lsum += p[P][i];
+        for (int hs = 0; hs < SP / 2; ++hs) {
+          pb[b][hs].x = pack_bf16x2(p[2 * hs][0], p[2 * hs][1]);
+          pb[b][hs].y = pack_bf16x2(p[2 * hs][2], p[2 * hs][3]);
+          pb[b][hs].z = pack_bf16x2(p[2 * hs + 1][0], p[2 * hs + 1][1]);
+          pb[b][hs].w = pack_bf16x2(p[2 * hs + 1][2], p[2 * hs + 1][3]);
         }
-      l[b] += lsum;
+      }
+
+      // O^T += V^T P^T, 32 keys (pages 2hs, 2hs+1) at a time.
 #pragma unroll
       for (int hs = 0; hs < SP / 2; ++hs) {
-        pb[b][hs].x = pack_bf16x2(p[2 * hs][0], p[2 * hs][1]);
-        pb[b][hs].y = pack_bf16x2(p[2 * hs][2], p[2 * hs][3]);
-        pb[b][hs].z = pack_bf16x2(p[2 * hs + 1][0], p[2 * hs + 1][1]);
-        pb[b][hs].w = pack_bf16x2(p[2 * hs + 1][2], p[2 * hs + 1][3]);
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const uint2 a = __builtin_bit_cast(uint2, read_tr(st + (SP + 2 * hs) * kTileBytes + voff[sl]));
+          const uint2 c = __builtin_bit_cast(uint2, read_tr(st + (SP + 2 * hs + 1) * kTileBytes + voff[sl]));
+          const uint4 v = make_uint4(a.x, a.y, c.x, c.y);
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            acc[b][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(v), as_bf16(pb[b][hs]),
+                                                                 acc[b][sl], 0, 0, 0);
+        }
       }
-    }
+    };
+    for (int s0 = 0; s0 < steps; s0 += RING)
+      static_for<RING>([&](auto i) {
+        if (s0 + decltype(i)::value < steps) step(s0 + decltype(i)::value, i);
+      });
 
-    // O^T += V^T P^T, 32 keys (pages 2hs, 2hs+1) at a time.
+    // Sum each column's l over its four lane groups, then write O and lse.
+    // Lane (nl, g4) holds dims 16 sl + 4 g4 + i of query nl.
 #pragma unroll
-    for (int hs = 0; hs < SP / 2; ++hs) {
+    for (int b = 0; b < 2; ++b) {
+      const float lt = col_sum(l[b]);
+      const int row = wrow0 + 16 * b + nl;
+      if (row >= row_hi) continue;
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const size_t rowh = (size_t)(q0 + row) * hq + h;
+      uint2 *orow = reinterpret_cast<uint2 *>(out + rowh * 128 + 4 * g4);
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) {
-        const uint2 a = __builtin_bit_cast(uint2, read_tr(st + (SP + 2 * hs) * kTileBytes + voff[sl]));
-        const uint2 c = __builtin_bit_cast(uint2, read_tr(st + (SP + 2 * hs + 1) * kTileBytes + voff[sl]));
-        const uint4 v = make_uint4(a.x, a.y, c.x, c.y);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[b][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(v), as_bf16(pb[b][hs]),
-                                                               acc[b][sl], 0, 0, 0);
-      }
+      for (int sl = 0; sl < 8; ++sl)
+        orow[4 * sl] = make_uint2(pack_bf16x2(acc[b][sl][0] * inv, acc[b][sl][1] * inv),
+                                  pack_bf16x2(acc[b][sl][2] * inv, acc[b][sl][3] * inv));
+      if (lse && g4 == 0) lse[rowh] = lt > 0.f ? (m[b] + log2f(lt)) * kLn2 : -INFINITY;
     }
-  };
-  for (int s0 = 0; s0 < steps; s0 += RING)
-    static_for<RING>([&](auto i) {
-      if (s0 + decltype(i)::value < steps) step(s0 + decltype(i)::value, i);
-    });
-
-  // Sum each column's l over its four lane groups, then write O and lse.
-  // Lane (nl, g4) holds dims 16 sl + 4 g4 + i of query nl.
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const float lt = col_sum(l[b]);
-    const int row = wrow0 + 16 * b + nl;
-    if (row >= row_hi) continue;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const size_t rowh = (size_t)(q0 + row) * hq + h;
-    uint2 *orow = reinterpret_cast<uint2 *>(out + rowh * 128 + 4 * g4);
-#pragma unroll
-    for (int sl = 0; sl < 8; ++sl)
-      orow[4 * sl] = make_uint2(pack_bf16x2(acc[b][sl][0] * inv, acc[b][sl][1] * inv),
-                                pack_bf16x2(acc[b][sl][2] * inv, acc[b][sl][3] * inv));
-    if (lse && g4 == 0) lse[rowh] = lt > 0.f ? (m[b] + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -405,7 +427,8 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
   const int tiles = (a.max_q_len + kTileRows - 1) / kTileRows;
   if (tiles == 0) return hipSuccess;
-  const long long blocks = (long long)tiles * a.num_q_heads * a.batch;
+  const long long units = (long long)a.num_q_heads * a.batch;
+  const long long blocks = (long long)((tiles + 1) / 2) * ((units + kXcds - 1) / kXcds * kXcds);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
