@@ -300,6 +300,24 @@ def test_prefill_ragged(dtype, hq, hkv, D):
     _prefill_compare(f"ragged/{dtype}/{hq}x{hkv}x{D}", case, chunks, gp, op)
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 16), (16, 2)])
+def test_prefill_tile_pairs(hq, hkv):
+    # the matrix-core prefill pairs each request's query tiles (T-1-p, p):
+    # ragged requests of 1, 2, 3, 5, 7 and 8 tiles of 128 rows in one call
+    # (odd counts leave a middle tile alone), q_lens that are not tile
+    # multiples, over cached prefixes, plus a request with nothing to do
+    say(f"prefill tile pairs {hq}/{hkv}")
+    prompts = [900, 200, 700, 600, 64, 1000, 100]
+    starts = [0, 0, 400, 20, 64, 150, 0]  # q_len 900, 200, 300, 580, 0, 850, 100: 8, 2, 3, 5, 0, 7, 1 tiles
+    case = synth.make_prefill_case(9, "bf16", prompts, hq, hkv, 128)
+    gp, op = gpu_pool(case.layout), oracle_pool(case.layout)
+    k, v, sl = synth.prefix_writes(case, starts)
+    write(gp, 0, 0, k, v, sl, "bf16")
+    oracle.kv_write(op, 0, 0, k, v, sl)
+    _prefill_compare(f"pairs/{hq}x{hkv}", case, synth.chunk_schedule(case, 4096, start=starts),
+                     gp, op)
+
+
 @pytest.mark.parametrize("lens,start", [([36000, 1000], [35800, 900]),
                                         ([70000], [69900])])
 def test_prefill_long_context(lens, start):
