@@ -262,8 +262,15 @@ class PrefillWorkload:
         return out
 
     def run(self, chunks, bank, write=True):
+        """write=True: paged_kv_write then paged_prefill_attn per chunk; False:
+        the attention alone; "extend": paged_extend_attn (one call)."""
         pkv = self.pkv
         for c in chunks:
+            if write == "extend":
+                pkv.extend(self.pool, bank, 0, c["k"], c["v"], c["slots"], c["q"], c["cu"],
+                           self.table_d, c["seq"], c["q_len"], c["hi"], out=c["o"],
+                           with_lse=False)
+                continue
             if write:
                 pkv.kv_write(self.pool, bank, 0, c["k"], c["v"], c["slots"])
             pkv.prefill(self.pool, bank, 0, c["q"], c["cu"], self.table_d, c["seq"], c["q_len"],
@@ -295,7 +302,7 @@ def run_prefill(reps=3, supplementary=True):
             wl.run(chunks, b)
         torch.cuda.synchronize()
         out = {}
-        for write in (True, False):
+        for write in (True, "extend", False):
             a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             nbk = wl.nb
             a.record()
@@ -304,7 +311,8 @@ def run_prefill(reps=3, supplementary=True):
             e.record()
             torch.cuda.synchronize()
             sec = a.elapsed_time(e) / 1e3 / (reps * nbk)
-            key = "write_then_attend" if write else "attend_only"
+            key = {True: "write_then_attend", "extend": "extend_one_call",
+                   False: "attend_only"}[write]
             out[key] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 2),
                         "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                         "hbm_GBps": round(hbm / sec / 1e9, 1)}

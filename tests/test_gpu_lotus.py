@@ -78,3 +78,40 @@ def test_lotus_passes(dtype, hq, hkv, D, prompts, block):
         assert np.array_equal(bits(out), bits(out2)) and np.array_equal(bits(lse), bits(lse2))
         assert np.array_equal(bits(gp.k), bits(gq.k)) and np.array_equal(bits(gp.v), bits(gq.v))
         check(f"lotus/pass{i}", dtype, out, ref[i][0], ref[i][1], lse)
+
+
+@pytest.mark.parametrize("chunk,start", [(2048, 0), (128, 0), (200, 37)])
+def test_extend_equals_write_then_prefill(chunk, start):
+    """paged_extend_attn over a chunk schedule equals paged_kv_write +
+    paged_prefill_attn bit for bit, pool included, and the oracle within
+    tolerance. Chunks of 2048 (four query tiles, paired), 128 (one tile over
+    earlier chunks) and 200 from position 37 (chunks that start and end
+    inside a page)."""
+    import torch
+
+    say(f"extend chunk={chunk} start={start}")
+    case = synth.make_prefill_case(5, "bf16", [512, 300, 450, 129], 16, 8, 128)
+    B = len(case.prompt_lens)
+    starts = [start] * B
+    chunks = synth.chunk_schedule(case, chunk, start=starts)
+    op = oracle_pool(case.layout)
+    ga, gb = gpu_pool(case.layout), gpu_pool(case.layout)
+    if start:
+        k, v, sl = synth.prefix_writes(case, starts)
+        oracle.kv_write(op, 0, 0, k, v, sl)
+        for g in (ga, gb):
+            write(g, 0, 0, k, v, sl, "bf16")
+    table = i32_dev(case.page_table)
+    for ci, ch in enumerate(chunks):
+        kd, vd, qd = to_dev(ch.k, "bf16"), to_dev(ch.v, "bf16"), to_dev(ch.q, "bf16")
+        sd, cu, seq = i32_dev(ch.slots), i32_dev(ch.cu_q_lens), i32_dev(ch.seq_lens)
+        mq, ms = int(np.diff(ch.cu_q_lens).max()), int(ch.seq_lens.max())
+        out_a, lse_a = pkv.extend(ga, 0, 0, kd, vd, sd, qd, cu, table, seq, mq, ms)
+        pkv.kv_write(gb, 0, 0, kd, vd, sd)
+        out_b, lse_b = pkv.prefill(gb, 0, 0, qd, cu, table, seq, mq, ms)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out_a), bits(out_b)) and np.array_equal(bits(lse_a), bits(lse_b))
+        assert np.array_equal(bits(ga.k), bits(gb.k)) and np.array_equal(bits(ga.v), bits(gb.v))
+        oracle.kv_write(op, 0, 0, ch.k, ch.v, ch.slots)
+        ro, rl = oracle.prefill(op, 0, 0, ch.q, ch.cu_q_lens, case.page_table, ch.seq_lens)
+        check(f"extend/c{chunk}/s{start}/{ci}", "bf16", out_a, ro, rl, lse_a)
