@@ -129,6 +129,34 @@ def traffic(args) -> dict:
     return res
 
 
+def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.4e9) -> list[dict]:
+    """Per launch shape of the kernels matching `kernel`: the mean of each
+    counter per dispatch and what follows from them. SQ_VALU_MFMA_BUSY_CYCLES
+    sums matrix-core busy clocks over every SIMD, so mfma_busy = that / (SIMDs
+    x dispatch time x the nominal 2.4 GHz engine clock), the fraction of the
+    dense MFMA peak the busy time could deliver."""
+    rows = csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv"))))
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for r in rows:
+        if kernel not in r["Kernel_Name"]:
+            continue
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+        acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur[key][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    out = []
+    for key, cs in sorted(acc.items()):
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        t = sum(dur[key].values()) / len(dur[key])
+        res = {"kernel": key[0], "grid": key[1], "dispatches": len(dur[key]), "us": t * 1e6, **m}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            res["mfma_busy"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * clock_hz * t)
+        if "SQ_INSTS_VALU" in m and m.get("SQ_INSTS_MFMA"):
+            res["valu_per_mfma"] = m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"]
+        out.append(res)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -139,6 +167,9 @@ def main(argv=None):
     sh.add_argument("dir")
     p = sub.add_parser("pmc")
     p.add_argument("dir")
+    e = sub.add_parser("engine")
+    e.add_argument("dir")
+    e.add_argument("--kernel", required=True)
     t = sub.add_parser("traffic")
     for k in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel"):
         t.add_argument(k, required=True)
@@ -164,6 +195,12 @@ def main(argv=None):
             print(k)
             for c, v in sorted(cs.items()):
                 print(f"    {c:40s} {v:.6g}")
+    elif args.cmd == "engine":
+        for r in engine_counters(args.dir, args.kernel):
+            print(f"{r['kernel']}  grid {r['grid']}  ({r['dispatches']} dispatches)")
+            for k, v in r.items():
+                if k not in ("kernel", "grid", "dispatches"):
+                    print(f"    {k:28s} {v:.6g}")
     else:
         res = traffic(args)
         text = json.dumps(res, indent=1)
