@@ -26,10 +26,13 @@
 // four (one workgroup per CU, longer contexts) the next three are. Each wave waits for its own copies with an
 // explicit vmcnt and one barrier per step publishes the stage (the compiler
 // does not track these copies, so the waits are written out). Within a
-// 256-byte token row the 16-byte chunk c of token t sits at c ^ rot(t)
-// (rot: 4-bit left rotation), which keeps both the K reads (16 tokens, one
-// chunk) and the transposing V reads (8 tokens, two chunks) free of bank
-// conflicts.
+// 256-byte token row the 16-byte chunk c of token t sits at c ^ t in a K
+// tile and at c ^ rot(t) in a V tile (rot: 4-bit left rotation). The
+// 16-byte K reads conflict as if LDS served them eight lanes at a time over
+// 32 four-byte banks: with the rotation on K, SQ_LDS_BANK_CONFLICT counted
+// four cycles per K read, and with the plain XOR it reads 0. The rotation
+// keeps the transposing 8-byte V reads (four tokens, two chunks per sixteen
+// lanes) conflict-free, where the plain XOR would not.
 //
 // Softmax: scores in base 2; the column max is a lane-swap reduction
 // (v_permlane32_swap, v_permlane16_swap); the output accumulators are
@@ -187,12 +190,15 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   // Copies: wave w moves tiles kTPW w .. kTPW w + kTPW - 1 of every stage
   // (tiles 0..SP-1 are the step's K pages, SP..2SP-1 its V pages), 1 KiB
   // (four token rows) per instruction; lane l of copy qq lands in LDS slot 64 qq + l, i.e. token
-  // 4 qq + l/16, swizzled chunk l%16, and so reads chunk (l%16) ^ rot(token).
+  // 4 qq + l/16, swizzled chunk l%16, and so reads chunk (l%16) ^ token (K tile) or
+  // (l%16) ^ rot(token) (V tile).
+  static_assert(SP % kTPW == 0, "a wave copies K tiles only or V tiles only");
+  const bool copies_k = kTPW * w < SP;
   uint32_t goff[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const int tt = 4 * qq + (lane >> 4);
-    goff[qq] = (uint32_t)(tt * 16 + ((lane & 15) ^ rot4(tt))) * 16u;
+    goff[qq] = (uint32_t)(tt * 16 + ((lane & 15) ^ (copies_k ? tt : rot4(tt)))) * 16u;
   }
   const uint32_t ring0 = lds_addr(ring);
   // Step j into ring slot `slot` (= j % RING, a compile-time constant).
@@ -214,10 +220,9 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
 
   // LDS read offsets within a tile. K: token nl, chunk 4c + g4. V (transposed
   // read for dims 16 sl .. +15): token 4 g4 + nl/4, dims 16 sl + 4 (nl%4) .. +3.
-  const int gk = rot4(nl);
   uint32_t koff[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) koff[c] = (uint32_t)(nl * 16 + ((4 * c + g4) ^ gk)) * 16u;
+  for (int c = 0; c < 4; ++c) koff[c] = (uint32_t)(nl * 16 + ((4 * c + g4) ^ nl)) * 16u;
   const int tv = 4 * g4 + (nl >> 2);
   const int gv = rot4(tv);
   uint32_t voff[8];
