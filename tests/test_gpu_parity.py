@@ -318,6 +318,34 @@ def test_prefill_tile_pairs(hq, hkv):
                      gp, op)
 
 
+def test_prefill_full_size_sampled():
+    """The 8 x 2048 cold prefill in the launch the benchmark prices (one
+    2048-token chunk of 8 prompts, 32 MHA heads, head_dim 128, written then
+    attended); the oracle checks prompts 0 and 5 on heads 0, 17 and 31, and
+    every output of the launch is finite."""
+    import torch
+
+    say("prefill full-size 8 x 2048")
+    case = synth.make_prefill_case(12, "bf16", [2048] * 8, 32, 32, 128)
+    chunks = synth.chunk_schedule(case, 2048)
+    assert len(chunks) == 1
+    out, lse = _prefill_gpu(case, chunks, gpu_pool(case.layout))[id(chunks[0])]
+    prompts, heads = [0, 5], [0, 17, 31]
+    sub = synth.PrefillCase(
+        synth.Layout("bf16", 16, case.layout.num_pages, len(heads), 128), len(heads),
+        case.prompt_lens[prompts], case.page_table[prompts],
+        [np.ascontiguousarray(case.k[r][:, heads]) for r in prompts],
+        [np.ascontiguousarray(case.v[r][:, heads]) for r in prompts],
+        [np.ascontiguousarray(case.q[r][:, heads]) for r in prompts], case.shared[prompts])
+    sc = synth.chunk_schedule(sub, 2048)
+    ro, rl = _prefill_oracle(sub, sc, oracle_pool(sub.layout))[id(sc[0])]
+    rows = torch.from_numpy(np.concatenate([np.arange(r * 2048, (r + 1) * 2048)
+                                            for r in prompts])).cuda()
+    hd = torch.tensor(heads, device="cuda")
+    check("full/8x2048", "bf16", out[rows][:, hd], ro, rl, lse[rows][:, hd])
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())
+
+
 @pytest.mark.parametrize("lens,start", [([36000, 1000], [35800, 900]),
                                         ([70000], [69900])])
 def test_prefill_long_context(lens, start):
