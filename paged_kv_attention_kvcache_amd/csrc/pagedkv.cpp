@@ -5,9 +5,11 @@
 
 #include <hip/hip_runtime.h>
 
-#include <cstdarg>
-#include <cstdio>
 #include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
 #include <cstring>
 
 #include "launch.hpp"
@@ -102,19 +104,20 @@ int check_heads(const pkv_pool *p, int32_t hq) {
   return PKV_OK;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; host threads may
+// race to fill an entry, with the same value).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Waves of the balanced split for this call: as many as are resident at once,
@@ -150,13 +153,15 @@ extern "C" {
 int pkv_bank_map(int32_t num_planes, int32_t num_layers, int32_t rec_first, int32_t rec_count,
                  int32_t *bank_of) {
   if (num_planes <= 0 || num_layers <= 0 || rec_first < 0 || rec_count < 0 ||
-      rec_first + rec_count > num_layers || !bank_of)
+      (int64_t)rec_first + rec_count > num_layers || !bank_of)
     return fail(PKV_EINVAL, "bad bank map request");
+  if ((int64_t)num_planes * num_layers > INT32_MAX)
+    return fail(PKV_EINVAL, "%d planes x %d layers is too many banks", num_planes, num_layers);
   int32_t next = 0;
   for (int32_t plane = 0; plane < num_planes; ++plane)
     for (int32_t layer = 0; layer < num_layers; ++layer) {
       const bool held = plane == 0 || (layer >= rec_first && layer < rec_first + rec_count);
-      bank_of[plane * num_layers + layer] = held ? next++ : -1;
+      bank_of[(size_t)plane * num_layers + layer] = held ? next++ : -1;
     }
   ok();
   return next;

@@ -66,6 +66,10 @@ def test_bank_map_matches_golden(L):
 def test_bank_map_rejects(L):
     with pytest.raises(pkv.PagedKVError):
         pkv.bank_map(2, 4, 3, 2)
+    # a recurrent range whose end overflows int32 is rejected, not wrapped
+    out = np.zeros(8, np.int32)
+    assert L.pkv_bank_map(2, 4, 3, 2**31 - 2, out.ctypes.data) == pkv.PKV_EINVAL
+    assert L.pkv_bank_map(2, 4, 1, -1, out.ctypes.data) == pkv.PKV_EINVAL
 
 
 def test_workspace_bytes(L):
