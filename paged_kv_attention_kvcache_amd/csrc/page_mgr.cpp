@@ -19,7 +19,9 @@
 // publication check is one comparison per plane.
 #include <algorithm>
 #include <cstdint>
+#include <climits>
 #include <functional>
+#include <memory>
 #include <vector>
 
 #include "launch.hpp"
@@ -54,16 +56,10 @@ void clear_page(pkv_page_mgr *m, int32_t page) {
   for (int32_t p = 0; p < m->num_planes; ++p) m->full[(size_t)p * m->num_pages + page] = 0;
 }
 
-}  // namespace
-
-extern "C" {
-
-pkv_page_mgr *pkv_mgr_create(int32_t num_pages, int32_t page_size, int32_t num_planes,
-                             int32_t num_layers, const int32_t *bank_of) {
-  if (num_pages <= 0 || page_size <= 0 || page_size > 64 || num_planes <= 0 ||
-      num_layers <= 0 || !bank_of)
-    return nullptr;
-  auto *m = new pkv_page_mgr;
+pkv_page_mgr *create_mgr(int32_t num_pages, int32_t page_size, int32_t num_planes,
+                         int32_t num_layers, const int32_t *bank_of) {
+  std::unique_ptr<pkv_page_mgr> holder(new pkv_page_mgr);
+  pkv_page_mgr *m = holder.get();
   m->num_pages = num_pages;
   m->page_size = page_size;
   m->num_planes = num_planes;
@@ -78,10 +74,7 @@ pkv_page_mgr *pkv_mgr_create(int32_t num_pages, int32_t page_size, int32_t num_p
     for (int32_t l = 0; l < num_layers; ++l) {
       const int32_t b = m->bank_of[(size_t)p * num_layers + l];
       if (b < 0) continue;
-      if (m->plane_of_bank[b] >= 0) {  // a bank belongs to one (plane, layer)
-        delete m;
-        return nullptr;
-      }
+      if (m->plane_of_bank[b] >= 0) return nullptr;  // a bank belongs to one (plane, layer)
       m->plane_of_bank[b] = p;
       ++m->held[p];
     }
@@ -91,9 +84,28 @@ pkv_page_mgr *pkv_mgr_create(int32_t num_pages, int32_t page_size, int32_t num_p
   m->mask.assign((size_t)nb * num_pages, 0);
   m->full.assign((size_t)num_planes * num_pages, 0);
   m->all = page_size == 64 ? ~0ull : ((1ull << page_size) - 1);
-  return m;
+  return holder.release();
 }
 
+}  // namespace
+
+extern "C" {
+
+pkv_page_mgr *pkv_mgr_create(int32_t num_pages, int32_t page_size, int32_t num_planes,
+                             int32_t num_layers, const int32_t *bank_of) {
+  if (num_pages <= 0 || page_size <= 0 || page_size > 64 || num_planes <= 0 ||
+      num_layers <= 0 || !bank_of || (int64_t)num_planes * num_layers > INT32_MAX)
+    return nullptr;
+  // A bank belongs to one (plane, layer), so ids run below planes x layers.
+  const int64_t max_banks = (int64_t)num_planes * num_layers;
+  for (int64_t i = 0; i < max_banks; ++i)
+    if (bank_of[i] >= max_banks) return nullptr;
+  try {
+    return create_mgr(num_pages, page_size, num_planes, num_layers, bank_of);
+  } catch (...) {  // out of host memory: nothing escapes the C interface
+    return nullptr;
+  }
+}
 void pkv_mgr_destroy(pkv_page_mgr *m) { delete m; }
 
 int32_t pkv_mgr_free_count(const pkv_page_mgr *m) {
@@ -125,11 +137,15 @@ int pkv_mgr_retain(pkv_page_mgr *m, int32_t n, const int32_t *page_ids) {
 int pkv_mgr_release(pkv_page_mgr *m, int32_t n, const int32_t *page_ids) {
   if (!m || !valid_ids(m, n, page_ids)) return mfail(PKV_EINVAL, "bad page ids");
   // all or nothing: no id may be released more times than it is held
-  std::vector<int32_t> ids(page_ids, page_ids + n);
-  std::sort(ids.begin(), ids.end());
-  for (int32_t i = 0, j = 0; i < n; i = j) {
-    while (j < n && ids[j] == ids[i]) ++j;
-    if (j - i > m->refs[ids[i]]) return mfail(PKV_EINVAL, "release of a free page");
+  try {
+    std::vector<int32_t> ids(page_ids, page_ids + n);
+    std::sort(ids.begin(), ids.end());
+    for (int32_t i = 0, j = 0; i < n; i = j) {
+      while (j < n && ids[j] == ids[i]) ++j;
+      if (j - i > m->refs[ids[i]]) return mfail(PKV_EINVAL, "release of a free page");
+    }
+  } catch (...) {
+    return mfail(PKV_EINVAL, "out of host memory");
   }
   for (int32_t i = 0; i < n; ++i)
     if (--m->refs[page_ids[i]] == 0) {

@@ -173,3 +173,16 @@ def test_library_errors():
     with pytest.raises(pkv.PagedKVError):
         m.retain([3])  # a free page
     m.close()
+
+
+def test_library_rejects_bad_bank_maps():
+    # a bank id at or past planes x layers, and one bank shared by two
+    # (plane, layer) entries, are refused at creation
+    bank_of = np.array([[0, 1], [2, 2**31 - 1]], np.int32)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.PageManager(4, bank_of, P)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.PageManager(4, np.array([[0, 1], [1, -1]], np.int32), P)
+    m = pkv.PageManager(4, np.array([[0, 1], [-1, 2]], np.int32), P)
+    assert m.free_count() == 4
+    m.close()
