@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <new>
 
 #include "launch.hpp"
 
@@ -375,7 +376,12 @@ int paged_decode_step_capture(const pkv_pool *pool, int32_t num_calls, const int
     (void)hipGraphDestroy(g);
     return fail(PKV_ELAUNCH, "hipGraphInstantiate failed: %s", hipGetErrorString(ei));
   }
-  *graph = new pkv_step_graph{g, x};
+  *graph = new (std::nothrow) pkv_step_graph{g, x};
+  if (!*graph) {
+    (void)hipGraphExecDestroy(x);
+    (void)hipGraphDestroy(g);
+    return fail(PKV_ELAUNCH, "out of host memory");
+  }
   return ok();
 }
 
