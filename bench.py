@@ -315,7 +315,8 @@ def run_prefill(reps=3, supplementary=True):
                    False: "attend_only"}[write]
             out[key] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 2),
                         "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "hbm_GBps": round(hbm / sec / 1e9, 1)}
+                        "hbm_GBps": round(hbm / sec / 1e9, 1),
+                        "hbm_frac": round(hbm / sec / 1e9 / HBM_PEAK_GBS, 4)}
         out["flops"] = flops
         out["algorithmic_bytes"] = hbm
         res[name] = out
@@ -409,6 +410,49 @@ def run_latest_bank(steps=10, warmup=2):
     return out
 
 
+def run_tiny(reps=500):
+    """The tiny decode shape (fp32, 4 requests of 17-64 tokens, 4 query / 2 kv
+    heads, head_dim 64, a 64-page pool): the fused store_kv + attention call,
+    timed per call. At about 166 KB of KV it measures launch latency, not
+    bandwidth."""
+    import torch
+
+    import paged_kv_attention_kvcache_amd as pkv
+    from paged_kv_attention_kvcache_amd import synth
+
+    case = synth.make_decode_case(0, "f32", 4, (17, 64), 4, 2, 64, num_pages=64)
+    bank_of, nb = pkv.bank_map(1, 1)
+    shape = (nb, 64, 2, 16, 64)
+    pool = pkv.Pool(torch.float32, 64, 2, 64, bank_of, nb,
+                    k=torch.zeros(shape, device="cuda"), v=torch.zeros(shape, device="cuda"))
+    bd = case.banks[(0, 0)]
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    pkv.kv_write(pool, 0, 0, dev(bd.fill_k), dev(bd.fill_v), dev(bd.fill_slots))
+    q, nk, nv = dev(bd.q), dev(bd.new_k), dev(bd.new_v)
+    table, seq = dev(case.page_table), dev(case.seq_lens)
+    mx = int(case.seq_lens.max())
+    ws = torch.empty(max(pkv.workspace_bytes(pool, 4, 4, mx, 0), 1), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((4, 4, 64), device="cuda")
+    lse = torch.empty((4, 4), device="cuda")
+    call = lambda: pkv.decode(pool, 0, 0, q, table, seq, mx, out=out, lse=lse, workspace=ws,
+                              k_new=nk, v_new=nv)
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    kv = int(case.seq_lens.sum()) * 2 * 2 * 64 * 4
+    return {"us_per_call": round(us, 3), "kv_bytes": kv, "kv_GBps": round(kv / us / 1e3, 2),
+            "how": "paged_decode_append_attn back to back on one stream (launch-bound)"}
+
+
 def run_page_mgr(reps=200):
     """Host bookkeeping of the page manager for one Huginn-shaped decode step
     (16 requests, 132 bank writes of one token each, then a publication
@@ -500,6 +544,17 @@ def run_decode(args):
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
+    # Per-step spread: K more steps, each between its own pair of events (after
+    # the timed region, so that region is K steps and nothing else).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for k in range(args.steps):
+        wl.step()
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])
+    spread = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
+
     # The decode calls alone, back to back over K rounds of every bank, between
     # two events on the stream the library launches on: the average duration
     # of the dominant kernel (its combine kernel included when the split
@@ -548,6 +603,7 @@ def run_decode(args):
         "data": "synthetic (seeded N(0,1) K/V/Q, random page permutation)",
         "config": dict(CONFIG_TEXT[wl.name], partition=wl.partition),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step_spread": spread,
         "tokens_planes_per_s": round(wl.batch * nb / (ms_per_step / 1e3), 1),
         "single_submission": {"ms_per_step": round(graph_ms, 4),
                               "kv_GBps": round(step_bytes / (graph_ms / 1e3) / 1e9, 2),
@@ -644,6 +700,11 @@ def main():
         res["prefill"] = run_prefill(supplementary=not args.no_supplementary)
         res["lotus"] = run_lotus()
         res["latest_bank"] = run_latest_bank()
+        res["tiny_decode"] = run_tiny()
+        torch.cuda.empty_cache()
+        res["hbm_probe"] = {k: run_probe(k)["GBps"] for k in ("copy", "read")}
+        res["hbm_probe"]["how"] = ("torch copy_ (read + write) and max (read) of 1 GiB: "
+                                   "the bandwidth a library kernel reaches")
     res["page_manager"] = run_page_mgr()
     print(json.dumps(res), flush=True)
 

@@ -43,6 +43,7 @@ constexpr int kDefaultPartition = 512;  // fixed partitions when the balanced sp
 constexpr int kStreamMaxBatch = 4096;   // rows the balanced split indexes in LDS
 constexpr int kWholeMaxSeq = 4096;      // longest context one workgroup reads whole
 constexpr int kWholeMinPairs = 512;     // (request, kv head) pairs that fill the GPU
+constexpr int kWholeShortSeq = 256;     // contexts this short take one launch at any batch
 constexpr size_t kAlign = 256;
 
 enum class Mode { kWhole, kStream, kFixed };
@@ -50,10 +51,13 @@ enum class Mode { kWhole, kStream, kFixed };
 // partition 0: one workgroup per (request, kv head) reading its whole
 // context when there are enough pairs to fill the GPU and contexts are short
 // (no partials, no combine launch, and requests that share prefix pages read
-// them at about the same time); otherwise the balanced split. partition > 0:
-// fixed partitions of that many tokens.
+// them at about the same time), or when every context is so short (at most
+// 16 pages) that the call is launch-bound and one launch beats the balanced
+// split's two; otherwise the balanced split. partition > 0: fixed partitions
+// of that many tokens.
 Mode decode_mode(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t partition) {
   if (partition > 0) return Mode::kFixed;
+  if (max_seq_len <= kWholeShortSeq) return Mode::kWhole;
   if (max_seq_len <= kWholeMaxSeq && (int64_t)batch * hkv >= kWholeMinPairs) return Mode::kWhole;
   return batch <= kStreamMaxBatch ? Mode::kStream : Mode::kFixed;
 }
