@@ -134,7 +134,8 @@ def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.
     counter per dispatch and what follows from them. SQ_VALU_MFMA_BUSY_CYCLES
     sums matrix-core busy clocks over every SIMD, so mfma_busy = that / (SIMDs
     x dispatch time x the nominal 2.4 GHz engine clock), the fraction of the
-    dense MFMA peak the busy time could deliver."""
+    dense MFMA peak the busy time could deliver; l2_hit = TCC_HIT / (TCC_HIT +
+    TCC_MISS), summed over the dies' L2 caches."""
     rows = csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv"))))
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     dur = collections.defaultdict(dict)
@@ -151,6 +152,8 @@ def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.
         res = {"kernel": key[0], "grid": key[1], "dispatches": len(dur[key]), "us": t * 1e6, **m}
         if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
             res["mfma_busy"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * clock_hz * t)
+        if m.get("TCC_HIT_sum", 0) + m.get("TCC_MISS_sum", 0) > 0:
+            res["l2_hit"] = m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])
         if "SQ_INSTS_VALU" in m and m.get("SQ_INSTS_MFMA"):
             res["valu_per_mfma"] = m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"]
         out.append(res)
