@@ -140,8 +140,9 @@ template <int SP, int RING, int MAXP>
 __global__ __launch_bounds__(kBlock) void prefill_mfma(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
     const uint16_t *__restrict__ q, int32_t hq, int32_t batch, int32_t tiles,
-    const int32_t *__restrict__ cu_q_lens, const int32_t *__restrict__ page_table,
-    int32_t pt_stride, const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale,
+    const int32_t *__restrict__ cu_q_lens, int32_t total_q,
+    const int32_t *__restrict__ page_table, int32_t pt_stride,
+    const int32_t *__restrict__ seq_lens, int32_t max_seq_len, float qscale,
     uint16_t *__restrict__ out, float *__restrict__ lse) {
   constexpr int kStepKeys = SP * kPage;
   constexpr int kStageBytes = 2 * SP * kTileBytes;  // K and V tiles of a step
@@ -170,9 +171,12 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
   if (slot / npairs >= per_xcd || unit >= hq * batch) return;
   const int h = unit % hq, r = unit / hq;
   const int kvh = h / (hq / hkv);
-  const int q0 = cu_q_lens[r];
+  // Rows stay inside the packed [total_q] arrays and the launched tiles
+  // whatever cu_q_lens holds.
+  const int q0 = min(max(cu_q_lens[r], 0), total_q);
   const int n = min(max(seq_lens[r], 0), max_seq_len);
-  const int q_len = min(max(cu_q_lens[r + 1] - q0, 0), n);
+  const int q_len = min(min(max(cu_q_lens[r + 1] - q0, 0), n),
+                        (int)min((long long)total_q - q0, (long long)tiles * kTileRows));
   const int tiles_r = (q_len + kTileRows - 1) / kTileRows;
   if (pr >= (tiles_r + 1) / 2) return;
   const int p0 = n - q_len;  // position of query row 0
@@ -439,8 +443,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kBlock), 0, stream,
                        static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                        a.bank.num_pages, a.bank.num_kv_heads, static_cast<const uint16_t *>(a.q),
-                       a.num_q_heads, a.batch, tiles, a.cu_q_lens, a.page_table, a.pt_stride,
-                       a.seq_lens, a.max_seq_len, a.scale * kLog2e,
+                       a.num_q_heads, a.batch, tiles, a.cu_q_lens, a.total_q, a.page_table,
+                       a.pt_stride, a.seq_lens, a.max_seq_len, a.scale * kLog2e,
                        static_cast<uint16_t *>(a.out), a.lse);
     return hipGetLastError();
   };
