@@ -1,0 +1,102 @@
+"""The rocprofv3 summaries behind the committed profiles, on small synthetic
+CSV files in rocprofv3's column layout (no GPU): kernel names, per-kernel and
+per-launch-shape times, counter averages, the HBM-traffic scaling by a copy
+of known size, and the engine figures (matrix-core busy fraction, L2 hit
+rate, VALU instructions per MFMA)."""
+from __future__ import annotations
+
+import csv
+import json
+import os
+
+import pytest
+
+from paged_kv_attention_kvcache_amd import rocprof_summary as rs
+
+DECODE = "void pkv::decode_whole<pkv::BF16, pkv::ValuFold<pkv::BF16, 128, 2, false>, 8>(uint4 const*, int)"
+COPY = "void at::native::copy_kernel<float>(float*, float const*)"
+
+
+def _write(path, header, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def _counters(d, rows):
+    """rows: (dispatch, kernel, grid, counter, value, start_ns, end_ns)."""
+    os.makedirs(d, exist_ok=True)
+    hdr = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value",
+           "Start_Timestamp", "End_Timestamp"]
+    _write(os.path.join(d, "run_counter_collection.csv"), hdr, rows)
+
+
+def test_short_name_keeps_templates_drops_arguments():
+    assert rs.short_name(DECODE) == \
+        "pkv::decode_whole<pkv::BF16, pkv::ValuFold<pkv::BF16, 128, 2, false>, 8>"
+    assert rs.short_name("void k(int)") == "k"
+    assert len(rs.short_name("x" * 300)) == 110
+
+
+def test_kernel_and_shape_stats(tmp_path):
+    d = str(tmp_path)
+    _write(os.path.join(d, "run_kernel_stats.csv"),
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+           [[DECODE, 4, 240000, 60000, 75.0, 58000, 62000]])
+    _write(os.path.join(d, "run_kernel_trace.csv"),
+           ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+            "End_Timestamp"],
+           [[DECODE, 131072, 1, 1, 0, 58000], [DECODE, 131072, 1, 1, 100000, 162000],
+            [DECODE, 65536, 1, 1, 200000, 230000]])
+    st = rs.kernel_stats(d)
+    assert st == [{"name": rs.short_name(DECODE), "calls": 4, "avg_us": 60.0, "min_us": 58.0,
+                   "max_us": 62.0, "pct": 75.0}]
+    sh = {r["grid"]: r for r in rs.shape_stats(d)}
+    assert sh[(131072, 1, 1)]["calls"] == 2 and sh[(131072, 1, 1)]["avg_us"] == 60.0
+    assert sh[(65536, 1, 1)]["min_us"] == 30.0
+
+
+def test_traffic_scales_by_the_copy_probe(tmp_path):
+    # a copy of 1 MiB reads 512 KiB of FETCH_SIZE (scale 2) and writes 1024
+    # KiB (scale 1); the kernel reads 1000 KiB and writes 10 KiB per dispatch
+    base = str(tmp_path)
+    _counters(os.path.join(base, "cf"), [[1, 256, COPY, "FETCH_SIZE", 512.0, 0, 10]])
+    _counters(os.path.join(base, "cw"), [[1, 256, COPY, "WRITE_SIZE", 1024.0, 0, 10]])
+    _counters(os.path.join(base, "kf"), [[1, 131072, DECODE, "FETCH_SIZE", 1000.0, 0, 10],
+                                         [2, 131072, DECODE, "FETCH_SIZE", 1000.0, 20, 30]])
+    _counters(os.path.join(base, "kw"), [[1, 131072, DECODE, "WRITE_SIZE", 10.0, 0, 10]])
+    out = os.path.join(base, "t.json")
+    rs.main(["traffic", "--fetch", os.path.join(base, "kf"), "--write", os.path.join(base, "kw"),
+             "--copy-fetch", os.path.join(base, "cf"), "--copy-write", os.path.join(base, "cw"),
+             "--kernel", "decode_whole", "--copy-bytes", str(1 << 20), "--json", out])
+    res = json.load(open(out))
+    assert res["fetch_scale"] == 2.0 and res["write_scale"] == 1.0
+    assert res["hbm_read_bytes_per_launch"] == 2000 * 1024
+    assert res["hbm_write_bytes_per_launch"] == 10 * 1024
+    assert res["kernel_source_hash"] == rs.kernel_source_hash()
+
+
+def test_engine_figures(tmp_path):
+    # one dispatch of 100 us: 1024 SIMDs x 2.4 GHz x 100 us = 245.76 M SIMD
+    # clocks, of which 61.44 M busy -> 25%; 300 of 400 L2 requests hit
+    d = str(tmp_path / "e")
+    rows = [[1, 524288, DECODE, c, v, 1000, 101000] for c, v in (
+        ("SQ_VALU_MFMA_BUSY_CYCLES", 61.44e6), ("SQ_INSTS_VALU", 390.0), ("SQ_INSTS_MFMA", 100.0),
+        ("TCC_HIT_sum", 300.0), ("TCC_MISS_sum", 100.0))]
+    _counters(d, rows)
+    (r,) = rs.engine_counters(d, "decode_whole")
+    assert r["grid"] == 524288 and r["dispatches"] == 1 and r["us"] == pytest.approx(100.0)
+    assert r["mfma_busy"] == pytest.approx(0.25)
+    assert r["l2_hit"] == pytest.approx(0.75)
+    assert r["valu_per_mfma"] == pytest.approx(3.9)
+    assert rs.engine_counters(d, "prefill") == []
+
+
+def test_source_hash_covers_decode_sources_only():
+    h = rs.kernel_source_hash()
+    assert len(h) == 16 and h == rs.kernel_source_hash()
+    names = sorted(n for n in os.listdir(os.path.join(rs.HERE, "csrc"))
+                   if n.endswith((".hip", ".hpp")))
+    assert "decode.hip" in names and "prefill_mfma.hip" in names
+    assert set(rs.NOT_DECODE) <= set(names)
