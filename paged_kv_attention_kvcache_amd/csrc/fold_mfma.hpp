@@ -19,14 +19,24 @@
 //                   P^T needs no data movement; V^T comes from 16-byte loads
 //                   of whole token rows (8 dims) transposed in registers.
 // Each lane ends with, for query n, the dims 32(l/16) .. +31.
+//
+// PC (per column): the 16 columns are up to 16 query rows of a short prefill
+// chunk (column n = query row n / gh of head kvh * gh + n % gh, gh = query
+// heads per kv head), each with its own causal end: column n sees keys below
+// col_hi. Keys at or past the context end still zero their V rows for every
+// column; keys inside the context but past a column's end only get
+// probability 0 in that column.
 #pragma once
+#include <climits>
+
 #include "span.hpp"
 
 namespace pkv {
 
-template <int G>
+template <int G, bool PC = false>
 struct MfmaFold {
-  static_assert(G == 4 || G == 8, "MFMA fold covers GQA groups of 4 and 8");
+  static_assert(PC ? G == 16 : (G == 4 || G == 8),
+                "MFMA fold covers GQA groups of 4 and 8, or 16 prefill columns");
   static constexpr int kPagesPerStep = 2;
   static constexpr bool kLatest = false;
   static constexpr int kDepth = 2;  // steps in flight per wave
@@ -47,6 +57,8 @@ struct MfmaFold {
   uint4 qb[4];  // B operand of S^T: query l%16, chunk 4c + l/16
   float qscale;
   int n, g4;
+  int ncols = G;                       // columns emitted
+  int col_hi = INT_MAX, hi_min = INT_MAX;  // PC: column n's key end; the smallest one
   uint32_t koff, voff;
   // Appended token (decode step): page index in the request, offset in the
   // page (-1: none), this lane's K chunks (as in Regs::k) and V chunk.
@@ -68,6 +80,26 @@ struct MfmaFold {
     for (int c = 0; c < 4; ++c)
       qb[c] = n < G ? *reinterpret_cast<const uint4 *>(qrow + n * 128 + (4 * c + g4) * 8)
                     : make_uint4(0, 0, 0, 0);
+  }
+
+  // PC: columns n < ncols are query rows q0 + n / gh, heads kvh * gh + n % gh
+  // of the packed q [rows][hq][128]; row j's keys end at p0 + j + 1.
+  __device__ __forceinline__ MfmaFold(const uint16_t *__restrict__ q, int q0, int hq, int kvh,
+                                      int gh, int cols, int p0, float qs)
+      : qscale(qs), ncols(cols), hi_min(p0 + 1) {
+    static_assert(PC, "the per-column constructor is for prefill columns");
+    const int lane = threadIdx.x & 63;
+    n = lane & 15;
+    g4 = lane >> 4;
+    koff = (uint32_t)(n * 256 + g4 * 16);
+    voff = (uint32_t)(g4 * 1024 + n * 16);
+    const int j = n / gh, g = n % gh;
+    col_hi = n < cols ? p0 + j + 1 : 0;
+    const uint16_t *qrow = q + ((size_t)(q0 + (n < cols ? j : 0)) * hq + (size_t)kvh * gh + g) * 128;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qb[c] = n < cols ? *reinterpret_cast<const uint4 *>(qrow + (4 * c + g4) * 8)
+                       : make_uint4(0, 0, 0, 0);
   }
 
   // Makes this wave the writer of the request's newest token at position pos:
@@ -152,15 +184,19 @@ struct MfmaFold {
       sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kk(0, c)), as_bf16(qb[c]), sA, 0, 0, 0);
       sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16(kk(1, c)), as_bf16(qb[c]), sB, 0, 0, 0);
     }
-    const bool full = piA >= 0 && piB >= 0 && piA * kPage >= lo && piA * kPage + kPage <= hi &&
-                      piB * kPage >= lo && piB * kPage + kPage <= hi;
+    // hf: keys below it are visible to every column; hc: this lane's column.
+    const int hf = PC ? min(hi, hi_min) : hi, hc = PC ? min(hi, col_hi) : hi;
+    const bool full = piA >= 0 && piB >= 0 && piA * kPage >= lo && piA * kPage + kPage <= hf &&
+                      piB * kPage >= lo && piB * kPage + kPage <= hf;
     float sv[8];
-    bool ok[8];
+    bool ok[8], in[8];  // ok: visible to this column; in: inside [lo, hi)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pa = piA * kPage + 4 * g4 + i, pb = piB * kPage + 4 * g4 + i;
-      ok[i] = full || (piA >= 0 && pa >= lo && pa < hi);
-      ok[4 + i] = full || (piB >= 0 && pb >= lo && pb < hi);
+      in[i] = full || (piA >= 0 && pa >= lo && pa < hi);
+      in[4 + i] = full || (piB >= 0 && pb >= lo && pb < hi);
+      ok[i] = PC ? (full || (in[i] && pa < hc)) : in[i];
+      ok[4 + i] = PC ? (full || (in[4 + i] && pb < hc)) : in[4 + i];
       sv[i] = ok[i] ? sA[i] * qscale : -INFINITY;
       sv[4 + i] = ok[4 + i] ? sB[i] * qscale : -INFINITY;
     }
@@ -194,7 +230,7 @@ struct MfmaFold {
     if (!full) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (!ok[e]) vr[e] = make_uint4(0, 0, 0, 0);
+        if (!in[e]) vr[e] = make_uint4(0, 0, 0, 0);
     }
     auto word = [](const uint4 &x, int w) { return w == 0 ? x.x : w == 1 ? x.y : w == 2 ? x.z : x.w; };
 #pragma unroll
@@ -218,7 +254,7 @@ struct MfmaFold {
 
   template <class Fn>
   __device__ __forceinline__ void emit(const State &st, Fn &&fn) const {
-    if (n >= G) return;
+    if (n >= (PC ? ncols : G)) return;
     float o[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i)

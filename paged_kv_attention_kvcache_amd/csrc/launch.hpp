@@ -85,5 +85,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // Matrix-core prefill (bf16, head_dim 128); launch_prefill picks it when it applies.
 bool prefill_mfma_supported(const PrefillArgs &a);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
+// Short chunks (bf16, head_dim 128, rows x GQA group <= 16 per request) as one
+// 16-column decode-style pass per (request, kv head); launch_prefill picks it first.
+bool prefill_cols_supported(const PrefillArgs &a);
+hipError_t launch_prefill_cols(const PrefillArgs &a, hipStream_t stream);
 
 }  // namespace pkv

@@ -82,6 +82,7 @@ static hipError_t prefill_by_group(const PrefillArgs &a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   if (a.total_q == 0) return hipSuccess;
+  if (prefill_cols_supported(a)) return launch_prefill_cols(a, stream);
   if (prefill_mfma_supported(a)) return launch_prefill_mfma(a, stream);
   if (a.bank.dtype == 1)
     return a.bank.head_dim == 128 ? prefill_by_group<BF16, 128>(a, stream)

@@ -32,7 +32,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # Sources the decode kernels are built from (the counter readings stored
 # for the decode workloads stay valid while these are unchanged).
-NOT_DECODE = ("prefill.hip", "prefill_mfma.hip", "kv_write.hip")
+NOT_DECODE = ("prefill.hip", "prefill_mfma.hip", "prefill_cols.hip", "kv_write.hip")
 
 
 def kernel_source_hash() -> str:

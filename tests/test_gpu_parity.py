@@ -290,6 +290,27 @@ def test_prefill_shared_prefix_suffix():
                      gp, op)
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 32), (16, 8), (16, 4), (16, 2)])
+def test_prefill_short_chunks(hq, hkv):
+    # chunks of at most 16 / group rows per request (bf16, head_dim 128) fold
+    # each (request, kv head) as one 16-column pass: ragged prompts of 1, 16,
+    # 17 tokens and page tails, cached prefixes, a request with no rows, and
+    # several chunks in a row
+    rows = 16 // (hq // hkv)
+    say(f"prefill short chunks {hq}/{hkv}: {rows} rows per request")
+    prompts = [512, 37, 1, 200, 16, 1000, 17, 300]
+    q_lens = [3 * rows, 2 * rows - 1, 1, rows + 1, 0, rows, 1, 2 * rows]
+    starts = [n - min(ql, n) for n, ql in zip(prompts, q_lens)]
+    case = synth.make_prefill_case(13, "bf16", prompts, hq, hkv, 128, q_scale=2.0)
+    gp, op = gpu_pool(case.layout), oracle_pool(case.layout)
+    k, v, sl = synth.prefix_writes(case, starts)
+    write(gp, 0, 0, k, v, sl, "bf16")
+    oracle.kv_write(op, 0, 0, k, v, sl)
+    chunks = synth.chunk_schedule(case, rows, start=starts)
+    assert len(chunks) == 3 and all(np.diff(c.cu_q_lens).max() <= rows for c in chunks)
+    _prefill_compare(f"short/{hq}x{hkv}", case, chunks, gp, op)
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,D", [("f32", 8, 2, 64), ("bf16", 8, 1, 128),
                                             ("f32", 2, 2, 128), ("bf16", 4, 2, 64)])
 def test_prefill_ragged(dtype, hq, hkv, D):

@@ -62,8 +62,10 @@ def test_decode_tables_out_of_contract(mode):
     assert out.shape == (batch, 16, 128) and lse.shape == (batch, 16)
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
-def test_prefill_tables_out_of_contract(dtype, D):
+@pytest.mark.parametrize("dtype,D,max_q", [("bf16", 128, 256), ("f32", 64, 256),
+                                           ("bf16", 128, 8)])
+def test_prefill_tables_out_of_contract(dtype, D, max_q):
+    # max_q 8 with a group of 2: the 16-column short-chunk kernel
     import torch
 
     rng = np.random.default_rng(43)
@@ -75,8 +77,8 @@ def test_prefill_tables_out_of_contract(dtype, D):
     seq = np.array([300, -5, 1 << 30, 17, 400], np.int32)
     table = _bad_table(rng, batch, stride, layout.num_pages)
     q = to_dev(synth.draw(rng, (total_q, 8, D), dtype), dtype)
-    say(f"prefill out-of-contract tables, {dtype} D={D}")
-    out, lse = pkv.prefill(pool, 0, 0, q, i32_dev(cu), i32_dev(table), i32_dev(seq), 256,
+    say(f"prefill out-of-contract tables, {dtype} D={D} max_q_len={max_q}")
+    out, lse = pkv.prefill(pool, 0, 0, q, i32_dev(cu), i32_dev(table), i32_dev(seq), max_q,
                            max_seq)
     torch.cuda.synchronize()
     assert np.array_equal(bits(pool.k), before[0]) and np.array_equal(bits(pool.v), before[1])
