@@ -25,6 +25,8 @@ constexpr int kColWaves = 4;  // the fold needs more than an 8-wave workgroup's 
 constexpr int kCols = 16;
 using ColFold = MfmaFold<kCols, true>;
 
+}  // namespace
+
 __global__ __launch_bounds__(64 * kColWaves) void prefill_cols(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
     const uint16_t *__restrict__ q, int32_t hq, const int32_t *__restrict__ cu_q_lens,
@@ -65,8 +67,6 @@ __global__ __launch_bounds__(64 * kColWaves) void prefill_cols(
                  A);
   }
 }
-
-}  // namespace
 
 bool prefill_cols_supported(const PrefillArgs &a) {
   const int gh = a.num_q_heads / a.bank.num_kv_heads;
