@@ -109,12 +109,7 @@ class DecodeWorkload:
         self.pkv = pkv
         self.separate_write = False
         self.split = pkv.split_mode(self.pool, batch, hq, self.max_seq, self.partition)
-        g = hq // hkv
-        fold = f"MfmaFold<{g}>" if g in (4, 8) and D == 128 else f"ValuFold<BF16, {D}, {g}>"
-        self.kernel_name = {
-            "whole": f"decode_whole<BF16, {fold}> (persistent, one launch per call)",
-            "balanced": f"decode_stream<BF16, {fold}> + decode_stream_combine",
-            "fixed": f"decode_block<BF16, {fold}> + decode_reduce"}[self.split]
+        self.kernel_name = self.kernel_for(self.split, self.partition)
         # algorithmic bytes: each request reads its whole context (K and V)
         self.kv_bytes_per_call = int(self.seq.astype(np.int64).sum()) * 2 * hkv * D * 2
         uniq_pages = len(np.unique(np.concatenate(
@@ -128,6 +123,51 @@ class DecodeWorkload:
             b = int(self.bank_of[order[i]])
             hb = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
             self.snap.append((hb(k[b])[None], hb(v[b])[None], hb(self.q[i])))
+
+    def kernel_for(self, split, partition):
+        """The decode kernels a call of this workload launches."""
+        g = self.hq // self.hkv
+        mfma = g in (4, 8) and self.D == 128
+        fold = f"MfmaFold<{g}>" if mfma else f"ValuFold<BF16, {self.D}, {g}>"
+        if split == "whole":
+            return f"decode_whole<BF16, {fold}> (persistent, one launch per call)"
+        if split == "balanced":
+            return f"decode_stream<BF16, {fold}> + decode_stream_combine"
+        pp = (partition or 512) // 16  # pages per partition (512 tokens by default)
+        parts = -(-self.max_seq // (partition or 512))
+        if parts > 1 and self.batch <= 4096 and pp % (2 if mfma else 1) == 0:
+            return f"decode_parts<BF16, {fold}> (persistent) + decode_reduce"
+        return f"decode_block<BF16, {fold}> + decode_reduce"
+
+    def time_fixed_partitions(self, partition, steps, stream):
+        """Decode calls (no fused append) on fixed partitions of `partition`
+        tokens and the in-order reduction, back to back between two events."""
+        import torch
+
+        pkv = self.pkv
+        wsb = pkv.workspace_bytes(self.pool, self.batch, self.hq, self.max_seq, partition)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        plane, layer = self.order[0]
+
+        def call():
+            pkv.decode(self.pool, plane, layer, self.q[0], self.table_d, self.seq_d,
+                       self.max_seq, partition=partition, out=self.out, lse=self.lse,
+                       workspace=ws)
+
+        call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        sec = a.elapsed_time(b) / 1e3 / steps
+        gbs = self.kv_bytes_per_call / sec / 1e9
+        return {"partition": partition, "us_per_call": round(sec * 1e6, 2),
+                "kv_GBps": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "kernel": self.kernel_for("fixed", partition),
+                "how": "paged_decode_attn alone (no fused append), back to back"}
 
     def use_exit_depths(self, lo, hi, seed=7):
         """Early exit: every context token halted at a depth drawn uniformly
@@ -621,6 +661,10 @@ def run_decode(args):
                      "kernel": wl.kernel_name},
         "wall_s_timed": round(wall, 3),
     }
+    if wl.name == "longctx" and wl.split != "fixed":
+        # the split this workload states: fixed 512-token partitions
+        res["fixed_partition_512"] = wl.time_fixed_partitions(512, args.steps, stream)
+        log(f"fixed partitions: {res['fixed_partition_512']}")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -281,6 +281,7 @@ static hipError_t decode_by_group(const DecodeArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (decode_parts_supported(a)) return launch_decode_parts(a, stream);
   if (a.bank.dtype == 1)
     return a.bank.head_dim == 128 ? decode_by_group<BF16, 128>(a, stream)
                                   : decode_by_group<BF16, 64>(a, stream);

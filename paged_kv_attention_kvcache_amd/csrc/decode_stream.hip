@@ -13,6 +13,8 @@
 // position order. The split depends only on the sequence lengths and the
 // grid size, so results are bitwise repeatable and independent of where the
 // pages live.
+#include <algorithm>
+
 #include "folds.hpp"
 #include "launch.hpp"
 
@@ -28,17 +30,17 @@ __device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t
   return w * total / nw;
 }
 
-// Block-wide exclusive prefix over rows of hkv * pages(r): cum[r] for r <= B
+// Block-wide exclusive prefix over rows of hkv * count(r): cum[r] for r <= B
 // (cum[B] = total), in LDS. Every thread of the block must call it.
-__device__ void row_prefix(const int32_t *__restrict__ seq_lens, int batch, int max_seq_len,
-                           int hkv, int *cum) {
+template <class Count>
+__device__ void row_prefix_of(Count count, int batch, int hkv, int *cum) {
   __shared__ int wave_tot[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (batch + kBlock - 1) / kBlock;
   const int r0 = tid * per;
   int sum = 0;
   for (int i = 0; i < per; ++i)
-    if (r0 + i < batch) sum += hkv * pages_of(seq_lens, r0 + i, max_seq_len);
+    if (r0 + i < batch) sum += hkv * count(r0 + i);
   int x = sum;  // inclusive scan over the wave
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -54,11 +56,17 @@ __device__ void row_prefix(const int32_t *__restrict__ seq_lens, int batch, int 
     const int r = r0 + i;
     if (r < batch) {
       cum[r] = run;
-      run += hkv * pages_of(seq_lens, r, max_seq_len);
+      run += hkv * count(r);
     }
   }
   if (tid == kBlock - 1) cum[batch] = run;
   __syncthreads();
+}
+
+// The prefix over rows of hkv * pages(r).
+__device__ __forceinline__ void row_prefix(const int32_t *__restrict__ seq_lens, int batch,
+                                           int max_seq_len, int hkv, int *cum) {
+  row_prefix_of([&](int r) { return pages_of(seq_lens, r, max_seq_len); }, batch, hkv, cum);
 }
 
 // Partial slot (wave, slot) of head g: (m, l) and acc[D].
@@ -246,6 +254,130 @@ __global__ __launch_bounds__(kBlock) void decode_stream_combine(
   }
 }
 
+// Fixed partitions, streamed. The work of a call is the sequence of
+// (request, kv head, partition) triples in request-major order; request r
+// owns hkv * max(1, ceil(n_r / partition)) of them (an empty context still
+// owns one, whose output is 0 and lse -inf). Every wave of a fully occupied
+// grid takes one contiguous, equal-sized range of partitions and folds their
+// pages as one pipelined stream per (request, kv head): at each partition end
+// the wave hands its state on as that partition's partial (or, for a context
+// of one partition, as the output) and starts the next from zero, so no
+// partition pays a start-up of its own. Each partition is folded by one wave
+// in page order, and decode_reduce then combines a row's partials in
+// partition order. Steps must not straddle partitions: the partition's pages
+// are a multiple of the fold's pages per step.
+__device__ __forceinline__ int parts_of(const int32_t *seq_lens, int r, int max_seq_len, int pp,
+                                        int max_parts) {
+  return min(max(1, (pages_of(seq_lens, r, max_seq_len) + pp - 1) / pp), max_parts);
+}
+
+template <typename E, class F>
+__global__ __launch_bounds__(kBlock) void decode_parts(
+    const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
+    const typename E::storage *__restrict__ q, int32_t hq,
+    const int32_t *__restrict__ page_table, int32_t pt_stride,
+    const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
+    int32_t partition, int32_t max_parts, typename E::storage *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ part_m, float *__restrict__ part_l,
+    float *__restrict__ part_acc, const typename E::storage *__restrict__ k_new,
+    const typename E::storage *__restrict__ v_new, uint4 *kb_w, uint4 *vb_w, LatestArgs la) {
+  constexpr int G = F::kGroup, D = F::kHeadDim;
+  extern __shared__ int cum[];  // [batch + 1]
+  // Per wave: a partial's acc, staged so that its global stores write whole
+  // 128-byte lines (a fold's lanes hold scattered 16-byte pieces of them).
+  // The staged lines are written with the nontemporal hint: in the middle of
+  // the page stream, cached writes of them cost measurably more.
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ f32x4 stage[kWaves][G * D / 4];
+  const int pp = partition / kPage;  // pages per partition
+  row_prefix_of([&](int r) { return parts_of(seq_lens, r, max_seq_len, pp, max_parts); }, batch,
+                hkv, cum);
+
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * kWaves + w;
+  const int64_t total = cum[batch];
+  int64_t s = range_start(gw, total, nw);
+  const int64_t e = range_start(gw + 1, total, nw);
+  if (s >= e) return;
+
+  // Row holding entry s: the first r with cum[r + 1] > s.
+  int lo_r = 0, hi_r = batch - 1;
+  while (lo_r < hi_r) {
+    const int mid = (lo_r + hi_r) >> 1;
+    if (cum[mid + 1] > s) hi_r = mid; else lo_r = mid + 1;
+  }
+  int r = lo_r;
+  int np = (cum[r + 1] - cum[r]) / hkv;
+  int kvh = (int)((s - cum[r]) / np);
+  int j = (int)((s - cum[r]) % np);
+  while (s < e) {
+    const int len = (int)min((int64_t)(np - j), e - s);  // partitions of this (r, kvh)
+    const int n = min(max(seq_lens[r], 0), max_seq_len);
+    const int p0 = j * pp, p1 = min((j + len) * pp, (n + kPage - 1) / kPage);
+    const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
+    F f(q + row0 * D, qscale);
+    if constexpr (F::kLatest) f.la = la;
+    typename F::State st;
+    f.reset(st);
+    const int32_t *pt_row = page_table + (size_t)r * pt_stride;
+    if (k_new && n > 0) {
+      const int pa = (n - 1) / kPage;  // page of the newest token
+      if (pa >= p0 && pa < p1)
+        f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
+                     n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
+    }
+    // Hands on the state of partition jj and starts the next one from zero.
+    auto hand = [&](int jj) {
+      f.finish_wave(st);
+      if (np == 1) {
+        emit_final<F, E>(f, st, out, lse, row0);
+      } else {
+        f32x4 *sw = stage[w];
+        f.emit(st, [&](int g, int d0, int cnt, float m, float l, const float *acc) {
+          for (int e2 = 0; e2 < cnt; e2 += 4)
+            sw[(g * D + d0 + e2) / 4] = f32x4{acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]};
+          if (d0 == 0) {
+            const size_t pj = (row0 + g) * max_parts + jj;
+            part_m[pj] = m;  // plain stores: measured faster here than nontemporal ones
+            part_l[pj] = l;
+          }
+        });
+        // The wave's LDS operations run in order, so its lanes read back
+        // what the others wrote; only the compiler must keep the order.
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        for (int i = lane; i < G * D / 4; i += 64) {
+          const int g = i / (D / 4), d = i % (D / 4) * 4;
+          __builtin_nontemporal_store(
+              sw[i], reinterpret_cast<f32x4 *>(part_acc + ((row0 + g) * max_parts + jj) * D + d));
+        }
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+      }
+      f.reset(st);
+    };
+    if (p1 > p0) {
+      const int cnt = p1 - p0;
+      stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p0, cnt, 1, 0, n,
+                   F::kLatest ? la.depth + (size_t)r * la.stride : nullptr, [&](int k) {
+                     if (k % pp == 0 || k == cnt) hand(j + (k - 1) / pp);
+                   });
+    } else {
+      hand(j);  // an empty context: its one partition has no pages
+    }
+    s += len;
+    j += len;
+    if (j == np) {
+      j = 0;
+      if (++kvh == hkv) {
+        kvh = 0;
+        if (++r < batch) np = (cum[r + 1] - cum[r]) / hkv;
+      }
+    }
+  }
+}
+
 // Workgroups per compute unit of the balanced split: as many as fit, or a
 // fixed count when built with -DPKV_STREAM_BLOCKS_PER_CU=n (tuning).
 template <typename E, int D, int G>
@@ -303,6 +435,87 @@ static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t str
                      a.max_seq_len, nw, reinterpret_cast<const float2 *>(a.part_m), a.part_acc,
                      static_cast<typename E::storage *>(a.out), a.lse);
   return hipGetLastError();
+}
+
+template <typename E, class F>
+static hipError_t parts_launch(const DecodeArgs &a, hipStream_t stream) {
+  static int per_cu = 0;  // resident workgroups per compute unit (cached)
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_parts<E, F>, kBlock, 0) !=
+            hipSuccess ||
+        nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  const int64_t units = (int64_t)a.batch * a.bank.num_kv_heads * a.max_parts;
+  const int64_t blocks = std::min<int64_t>((int64_t)a.num_cus * per_cu, (units + kWaves - 1) / kWaves);
+  const size_t lds = sizeof(int) * ((size_t)a.batch + 1);
+  hipLaunchKernelGGL((decode_parts<E, F>), dim3((unsigned)blocks), dim3(kBlock), lds, stream,
+                     static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
+                     a.bank.num_pages, a.bank.num_kv_heads,
+                     static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
+                     a.pt_stride, a.seq_lens, a.batch, a.max_seq_len, a.scale * kLog2e,
+                     a.partition, a.max_parts, static_cast<typename E::storage *>(a.out), a.lse,
+                     a.part_m, a.part_l, a.part_acc,
+                     static_cast<const typename E::storage *>(a.k_new),
+                     static_cast<const typename E::storage *>(a.v_new),
+                     static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v), a.latest);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, F::kHeadDim, a.seq_lens,
+                       a.max_seq_len, a.partition, a.max_parts, a.part_m, a.part_l, a.part_acc,
+                       a.out, a.lse, true, stream);
+}
+
+template <typename E, int D>
+static hipError_t parts_by_group(const DecodeArgs &a, hipStream_t stream) {
+  if (a.latest.depth) {
+    switch (a.num_q_heads / a.bank.num_kv_heads) {
+      case 1: return parts_launch<E, ValuFold<E, D, 1, true>>(a, stream);
+      case 2: return parts_launch<E, ValuFold<E, D, 2, true>>(a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (a.num_q_heads / a.bank.num_kv_heads) {
+    case 1: return parts_launch<E, typename FoldFor<E, D, 1>::type>(a, stream);
+    case 2: return parts_launch<E, typename FoldFor<E, D, 2>::type>(a, stream);
+    case 4: return parts_launch<E, typename FoldFor<E, D, 4>::type>(a, stream);
+    case 8: return parts_launch<E, typename FoldFor<E, D, 8>::type>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E, int D>
+static int pages_per_step(int group, bool latest) {
+  if (latest) return 1;
+  switch (group) {
+    case 1: return FoldFor<E, D, 1>::type::kPagesPerStep;
+    case 2: return FoldFor<E, D, 2>::type::kPagesPerStep;
+    case 4: return FoldFor<E, D, 4>::type::kPagesPerStep;
+    case 8: return FoldFor<E, D, 8>::type::kPagesPerStep;
+  }
+  return 0;
+}
+
+bool decode_parts_supported(const DecodeArgs &a) {
+  const int g = a.num_q_heads / a.bank.num_kv_heads;
+  const bool latest = a.latest.depth != nullptr;
+  const int s = a.bank.dtype == 1
+                    ? (a.bank.head_dim == 128 ? pages_per_step<BF16, 128>(g, latest)
+                                              : pages_per_step<BF16, 64>(g, latest))
+                    : (a.bank.head_dim == 128 ? pages_per_step<F32, 128>(g, latest)
+                                              : pages_per_step<F32, 64>(g, latest));
+  return a.max_parts > 1 && a.batch <= kPartsMaxBatch && s > 0 && a.partition % kPage == 0 &&
+         (a.partition / kPage) % s == 0;
+}
+
+hipError_t launch_decode_parts(const DecodeArgs &a, hipStream_t stream) {
+  if (a.bank.dtype == 1)
+    return a.bank.head_dim == 128 ? parts_by_group<BF16, 128>(a, stream)
+                                  : parts_by_group<BF16, 64>(a, stream);
+  return a.bank.head_dim == 128 ? parts_by_group<F32, 128>(a, stream)
+                                : parts_by_group<F32, 64>(a, stream);
 }
 
 template <typename E, int D>

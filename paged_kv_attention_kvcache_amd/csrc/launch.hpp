@@ -56,6 +56,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeArgs &a, int64_t nw, hipStream_t stream);
 // Waves of the stream kernel that fit on num_cus compute units at once.
 int stream_waves(int dtype, int head_dim, int group, int num_cus);
+// Fixed partitions streamed by a persistent grid (one wave per partition,
+// then decode_reduce); launch_decode takes it whenever it applies.
+constexpr int kPartsMaxBatch = 4096;  // rows whose prefix the kernel keeps in LDS
+bool decode_parts_supported(const DecodeArgs &a);
+hipError_t launch_decode_parts(const DecodeArgs &a, hipStream_t stream);
 
 hipError_t launch_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads,
                          int32_t head_dim, const int32_t *seq_lens,

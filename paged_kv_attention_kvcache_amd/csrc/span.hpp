@@ -20,16 +20,24 @@ namespace pkv {
 constexpr int kWaves = 4;
 constexpr int kBlock = 64 * kWaves;
 
+// No action after a step (stream_pages' default).
+struct NoStepHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 // Streams `count` pages p_first + stride * k (k = 0 .. count-1) of one
-// (request, kv head) through fold f; keys outside [lo, hi) are masked.
-template <class F>
+// (request, kv head) through fold f; keys outside [lo, hi) are masked. After
+// each step, after(k) runs with k = the pages folded so far (a multiple of
+// F::kPagesPerStep, or count); it may hand the state on and reset it.
+template <class F, class After = NoStepHook>
 __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
                                              const uint4 *__restrict__ kb,
                                              const uint4 *__restrict__ vb,
                                              const int32_t *__restrict__ pt_row,
                                              int32_t num_pages, int32_t hkv, int32_t kvh,
                                              int p_first, int count, int stride, int lo, int hi,
-                                             const uint8_t *__restrict__ ex_row = nullptr) {
+                                             const uint8_t *__restrict__ ex_row = nullptr,
+                                             After after = After()) {
   constexpr int S = F::kPagesPerStep;
   const int lane = threadIdx.x & 63;
   for (int base = 0; base < count; base += 64) {
@@ -66,6 +74,7 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
     auto fold = [&](typename F::Regs &r, int s) {
       f.fold(st, r, index(s * S), S > 1 ? index(s * S + 1) : -1, lo, hi);
       asm volatile("" ::: "memory");
+      after(base + min(s * S + S, cnt));
     };
     if constexpr (F::kDepth >= 3) {
       // Three steps in flight: the steady state (all prefetches exist) runs

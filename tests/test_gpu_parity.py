@@ -195,6 +195,28 @@ def test_decode_edge_lengths(partition):
     assert np.all(f64(out)[0] == 0) and np.all(f64(lse)[0] == -np.inf)
 
 
+@pytest.mark.parametrize("hq,hkv,partition", [(64, 8, 32), (64, 8, 48), (8, 8, 48), (16, 2, 512)])
+def test_decode_fixed_partitions(hq, hkv, partition):
+    # fixed partitions run on a persistent grid that streams them, one wave
+    # per partition, when a partition holds a whole number of the fold's steps
+    # (two pages for the matrix-core fold of groups 4 and 8), else one
+    # workgroup per partition (48 tokens with group 8). 40 requests, so waves
+    # cross request boundaries; lengths at, one below and one past partition
+    # multiples, empty and one-token rows.
+    rng = np.random.default_rng(17)
+    P = partition
+    lens = [int(x) for x in rng.integers(0, 3000, size=28)] + \
+        [0, 1, P - 1, P, P + 1, 2 * P, 2 * P + 1, 3 * P - 1, 16, 17, 4095, 4096]
+    say(f"decode fixed partitions {hq}/{hkv} partition={P}")
+    case = synth.make_decode_case(7, "bf16", len(lens), (0, 0), hq, hkv, 128, seq_lens=lens)
+    assert pkv.split_mode(gpu_pool(case.layout), len(lens), hq, max(lens), P) == "fixed"
+    ro, rl, _ = oracle_decode_case(case)
+    out, lse, _ = gpu_decode_case(case, partition=P)
+    check(f"fixed/{hq}x{hkv}/p{P}", "bf16", out, ro, rl, lse)
+    zero = [i for i, n in enumerate(lens) if n == 0]
+    assert np.all(f64(out)[zero] == 0) and np.all(f64(lse)[zero] == -np.inf)
+
+
 def test_decode_edge_lengths_whole():
     # the same edge lengths in whole-context mode (64 requests x 8 kv heads)
     lens = [0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000] * 5 + [0, 2, 4095, 4096]
@@ -436,8 +458,11 @@ FULL = {
     "c2_full": dict(B=64, lo=512, hi=2048, hq=16, hkv=8, alias=0.0, rows=[0, 31, 63]),
     # config 3: Huginn, 78% aliased prompts
     "c3_full": dict(B=16, lo=200, hi=2000, hq=32, hkv=32, alias=0.78, rows=[0, 7, 15]),
-    # config 5: 256 requests, 8k-32k context, GQA 8, split-K over 512
+    # config 5: 256 requests, 8k-32k context, GQA 8; the library's balanced
+    # split and the stated split-K over fixed 512-token partitions
     "c5_full": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255]),
+    "c5_full_p512": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255],
+                         partition=512),
 }
 
 
@@ -479,7 +504,8 @@ def test_full_size_sampled(name):
     ro, rl = oracle.decode(opool, 0, 0, bits(q)[rows], otable, seq[rows])
     # the GPU path: write the new token, then decode, as the benchmark does
     pkv.kv_write(pool, 0, 0, nk, nv, i32_dev(slots))
-    out, lse = pkv.decode(pool, 0, 0, q, i32_dev(table), i32_dev(seq), int(seq.max()))
+    out, lse = pkv.decode(pool, 0, 0, q, i32_dev(table), i32_dev(seq), int(seq.max()),
+                          partition=f.get("partition", 0))
     torch.cuda.synchronize()
     check(name, "bf16", f64(out)[rows], ro, rl, lse[rows])
     # every row of the full batch is finite (no stray read of poison or of
