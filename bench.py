@@ -136,7 +136,7 @@ class DecodeWorkload:
         pp = (partition or 512) // 16  # pages per partition (512 tokens by default)
         parts = -(-self.max_seq // (partition or 512))
         if parts > 1 and self.batch <= 4096 and pp % (2 if mfma else 1) == 0:
-            return f"decode_parts<BF16, {fold}> (persistent) + decode_reduce"
+            return f"decode_parts<BF16, {fold}> (persistent) + decode_parts_combine"
         return f"decode_block<BF16, {fold}> + decode_reduce"
 
     def time_fixed_partitions(self, partition, steps, stream):

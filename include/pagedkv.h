@@ -132,8 +132,17 @@ size_t paged_decode_workspace_bytes(const pkv_pool *pool, int32_t batch,
  * Work split (the fp32 partials (m, l, acc) of a split context are folded in
  * position order by a combine kernel, so results are bitwise repeatable and
  * independent of physical page placement):
- *   partition > 0 (a multiple of 16): fixed partitions of that many tokens,
- *     one workgroup per (partition, kv head, request).
+ *   partition > 0 (a multiple of 16): fixed partitions of that many tokens.
+ *     Each partition is folded from a fresh state, and a row's partitions
+ *     are combined in partition order with the fp32 merge (rescale each to
+ *     the larger max). When a partition holds a whole number of the fold's
+ *     steps (two pages for bf16 head_dim 128 with GQA groups 4 and 8, one
+ *     page otherwise) and batch <= 4096, a persistent grid deals the
+ *     partitions to its waves in equal contiguous ranges and merges each
+ *     row's partitions in registers (rows split between waves are finished
+ *     by a combine kernel); otherwise one workgroup per (partition, kv head,
+ *     request) writes partials that a reduction combines as
+ *     paged_decode_reduce does.
  *   partition 0 (library default), chosen per call:
  *     - whole contexts, one workgroup per (request, kv head), when
  *       batch * num_kv_heads >= 512 and max_seq_len <= 4096 (no partials,
@@ -267,7 +276,7 @@ void paged_decode_step_graph_destroy(pkv_step_graph *graph);
  * part_acc = sum 2^(log2(e) s - part_m) V. Output:
  *   M = max_j m_j, L = sum_j l_j 2^(m_j - M), out = sum_j acc_j 2^(m_j - M) / L,
  *   lse = ln(2) (M + log2 L).
- * The arrays are laid out as in the workspace (rows x max_parts [x head_dim]).
+ * The arrays are laid out rows x max_parts [x head_dim].
  * A row with no partial gets out 0, lse -inf. */
 int paged_decode_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads,
                         int32_t head_dim, const int32_t *seq_lens,

@@ -25,6 +25,12 @@ __device__ __forceinline__ int pages_of(const int32_t *seq_lens, int r, int max_
   return (n + kPage - 1) / kPage;
 }
 
+// Partitions of request r (an empty context owns one).
+__device__ __forceinline__ int parts_of(const int32_t *seq_lens, int r, int max_seq_len, int pp,
+                                        int max_parts) {
+  return min(max(1, (pages_of(seq_lens, r, max_seq_len) + pp - 1) / pp), max_parts);
+}
+
 // First entry of the range of wave w, for `total` entries over `nw` waves.
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t nw) {
   return w * total / nw;
@@ -155,19 +161,21 @@ __global__ __launch_bounds__(kBlock) void decode_stream(
 // in LDS, so each thread's acc loads are independent of one another.
 constexpr int kSegChunk = 64;
 
-template <typename E, int G>
-__global__ __launch_bounds__(kBlock) void decode_stream_combine(
-    int32_t hkv, int32_t D, const int32_t *__restrict__ seq_lens, int32_t batch,
-    int32_t max_seq_len, int64_t nw, const float2 *__restrict__ part_ml,
-    const float *__restrict__ part_acc, typename E::storage *__restrict__ out,
-    float *__restrict__ lse) {
+// The units of row r are count(r) entries per kv head (pages for the
+// balanced split, partitions for decode_parts).
+template <typename E, int G, class Count>
+__device__ __forceinline__ void combine_units(Count count, int32_t hkv, int32_t D, int32_t batch,
+                                              int64_t nw, const float2 *__restrict__ part_ml,
+                                              const float *__restrict__ part_acc,
+                                              typename E::storage *__restrict__ out,
+                                              float *__restrict__ lse) {
   __shared__ int sums[2][kBlock];
   __shared__ int seg_part[kSegChunk];  // part_index(wave, slot, G, 0) / G
   __shared__ float2 seg_ml[kSegChunk][G];
   const int u = blockIdx.x, r = u / hkv, kvh = u % hkv, tid = threadIdx.x;
   int before = 0, all = 0;
   for (int i = tid; i < batch; i += kBlock) {
-    const int v = hkv * pages_of(seq_lens, i, max_seq_len);
+    const int v = hkv * count(i);
     all += v;
     if (i < r) before += v;
   }
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void decode_stream_combine(
     __syncthreads();
   }
   const int64_t total = sums[1][0];
-  const int pr = pages_of(seq_lens, r, max_seq_len);
+  const int pr = count(r);
   const int64_t a = (int64_t)sums[0][0] + (int64_t)kvh * pr, b = a + pr;
   const size_t row0 = (size_t)r * hkv * G + (size_t)kvh * G;
   if (pr == 0) {
@@ -254,23 +262,42 @@ __global__ __launch_bounds__(kBlock) void decode_stream_combine(
   }
 }
 
+template <typename E, int G>
+__global__ __launch_bounds__(kBlock) void decode_stream_combine(
+    int32_t hkv, int32_t D, const int32_t *__restrict__ seq_lens, int32_t batch,
+    int32_t max_seq_len, int64_t nw, const float2 *__restrict__ part_ml,
+    const float *__restrict__ part_acc, typename E::storage *__restrict__ out,
+    float *__restrict__ lse) {
+  combine_units<E, G>([&](int r) { return pages_of(seq_lens, r, max_seq_len); }, hkv, D, batch,
+                      nw, part_ml, part_acc, out, lse);
+}
+
+// The combine of decode_parts: a (request, kv head)'s segments in wave order.
+template <typename E, int G>
+__global__ __launch_bounds__(kBlock) void decode_parts_combine(
+    int32_t hkv, int32_t D, const int32_t *__restrict__ seq_lens, int32_t batch,
+    int32_t max_seq_len, int32_t partition, int32_t max_parts, int64_t nw,
+    const float2 *__restrict__ part_ml, const float *__restrict__ part_acc,
+    typename E::storage *__restrict__ out, float *__restrict__ lse) {
+  const int pp = partition / kPage;
+  combine_units<E, G>([&](int r) { return parts_of(seq_lens, r, max_seq_len, pp, max_parts); },
+                      hkv, D, batch, nw, part_ml, part_acc, out, lse);
+}
+
 // Fixed partitions, streamed. The work of a call is the sequence of
 // (request, kv head, partition) triples in request-major order; request r
 // owns hkv * max(1, ceil(n_r / partition)) of them (an empty context still
 // owns one, whose output is 0 and lse -inf). Every wave of a fully occupied
 // grid takes one contiguous, equal-sized range of partitions and folds their
-// pages as one pipelined stream per (request, kv head): at each partition end
-// the wave hands its state on as that partition's partial (or, for a context
-// of one partition, as the output) and starts the next from zero, so no
-// partition pays a start-up of its own. Each partition is folded by one wave
-// in page order, and decode_reduce then combines a row's partials in
-// partition order. Steps must not straddle partitions: the partition's pages
-// are a multiple of the fold's pages per step.
-__device__ __forceinline__ int parts_of(const int32_t *seq_lens, int r, int max_seq_len, int pp,
-                                        int max_parts) {
-  return min(max(1, (pages_of(seq_lens, r, max_seq_len) + pp - 1) / pp), max_parts);
-}
-
+// pages as one pipelined stream per (request, kv head). Each partition is
+// folded from a fresh state by one wave, in page order; at its end the wave
+// combines it into the (request, kv head)'s running result in partition
+// order (the fp32 split-K reduction), so no partition's partial leaves the
+// registers. A (request, kv head) inside one wave's range is finished by that
+// wave; one split between waves leaves a partial per wave (at most two per
+// wave, slots 0 and 1, as in the balanced split) for decode_parts_combine.
+// Steps must not straddle partitions: a partition's pages are a multiple of
+// the fold's pages per step.
 template <typename E, class F>
 __global__ __launch_bounds__(kBlock) void decode_parts(
     const uint4 *__restrict__ kb, const uint4 *__restrict__ vb, int32_t num_pages, int32_t hkv,
@@ -278,24 +305,17 @@ __global__ __launch_bounds__(kBlock) void decode_parts(
     const int32_t *__restrict__ page_table, int32_t pt_stride,
     const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
     int32_t partition, int32_t max_parts, typename E::storage *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_acc, const typename E::storage *__restrict__ k_new,
-    const typename E::storage *__restrict__ v_new, uint4 *kb_w, uint4 *vb_w, LatestArgs la) {
+    float *__restrict__ lse, float2 *__restrict__ part_ml, float *__restrict__ part_acc,
+    const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
+    uint4 *kb_w, uint4 *vb_w, LatestArgs la) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   extern __shared__ int cum[];  // [batch + 1]
-  // Per wave: a partial's acc, staged so that its global stores write whole
-  // 128-byte lines (a fold's lanes hold scattered 16-byte pieces of them).
-  // The staged lines are written with the nontemporal hint: in the middle of
-  // the page stream, cached writes of them cost measurably more.
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __shared__ f32x4 stage[kWaves][G * D / 4];
   const int pp = partition / kPage;  // pages per partition
   row_prefix_of([&](int r) { return parts_of(seq_lens, r, max_seq_len, pp, max_parts); }, batch,
                 hkv, cum);
 
   const int64_t nw = (int64_t)gridDim.x * kWaves;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * kWaves + w;
+  const int64_t gw = (int64_t)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t total = cum[batch];
   int64_t s = range_start(gw, total, nw);
   const int64_t e = range_start(gw + 1, total, nw);
@@ -311,6 +331,7 @@ __global__ __launch_bounds__(kBlock) void decode_parts(
   int np = (cum[r + 1] - cum[r]) / hkv;
   int kvh = (int)((s - cum[r]) / np);
   int j = (int)((s - cum[r]) % np);
+  int slot = 0;
   while (s < e) {
     const int len = (int)min((int64_t)(np - j), e - s);  // partitions of this (r, kvh)
     const int n = min(max(seq_lens[r], 0), max_seq_len);
@@ -318,8 +339,9 @@ __global__ __launch_bounds__(kBlock) void decode_parts(
     const size_t row0 = (size_t)r * hq + (size_t)kvh * G;
     F f(q + row0 * D, qscale);
     if constexpr (F::kLatest) f.la = la;
-    typename F::State st;
+    typename F::State st, run;
     f.reset(st);
+    f.reset(run);  // the combine of no partition: m = -inf, l = 0, acc = 0
     const int32_t *pt_row = page_table + (size_t)r * pt_stride;
     if (k_new && n > 0) {
       const int pa = (n - 1) / kPage;  // page of the newest token
@@ -327,46 +349,30 @@ __global__ __launch_bounds__(kBlock) void decode_parts(
         f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
                      n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
     }
-    // Hands on the state of partition jj and starts the next one from zero.
-    auto hand = [&](int jj) {
-      f.finish_wave(st);
-      if (np == 1) {
-        emit_final<F, E>(f, st, out, lse, row0);
-      } else {
-        f32x4 *sw = stage[w];
-        f.emit(st, [&](int g, int d0, int cnt, float m, float l, const float *acc) {
-          for (int e2 = 0; e2 < cnt; e2 += 4)
-            sw[(g * D + d0 + e2) / 4] = f32x4{acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]};
-          if (d0 == 0) {
-            const size_t pj = (row0 + g) * max_parts + jj;
-            part_m[pj] = m;  // plain stores: measured faster here than nontemporal ones
-            part_l[pj] = l;
-          }
-        });
-        // The wave's LDS operations run in order, so its lanes read back
-        // what the others wrote; only the compiler must keep the order.
-        __builtin_amdgcn_wave_barrier();
-        asm volatile("" ::: "memory");
-        for (int i = lane; i < G * D / 4; i += 64) {
-          const int g = i / (D / 4), d = i % (D / 4) * 4;
-          __builtin_nontemporal_store(
-              sw[i], reinterpret_cast<f32x4 *>(part_acc + ((row0 + g) * max_parts + jj) * D + d));
-        }
-        __builtin_amdgcn_wave_barrier();
-        asm volatile("" ::: "memory");
-      }
-      f.reset(st);
-    };
     if (p1 > p0) {
       const int cnt = p1 - p0;
       stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, p0, cnt, 1, 0, n,
                    F::kLatest ? la.depth + (size_t)r * la.stride : nullptr, [&](int k) {
-                     if (k % pp == 0 || k == cnt) hand(j + (k - 1) / pp);
+                     if (k % pp == 0 || k == cnt) {  // a partition ends
+                       f.finish_wave(st);
+                       F::merge(run, st);
+                       f.reset(st);
+                     }
                    });
+    }
+    if (j == 0 && len == np) {  // the whole (request, kv head): finish here
+      emit_final<F, E>(f, run, out, lse, row0);
     } else {
-      hand(j);  // an empty context: its one partition has no pages
+      f.emit(run, [&](int g, int d0, int c, float m, float l, const float *acc) {
+        const size_t pi = part_index(gw, slot, G, g);
+        for (int e2 = 0; e2 < c; e2 += 4)
+          *reinterpret_cast<float4 *>(part_acc + pi * D + d0 + e2) =
+              make_float4(acc[e2], acc[e2 + 1], acc[e2 + 2], acc[e2 + 3]);
+        if (d0 == 0) part_ml[pi] = make_float2(m, l);
+      });
     }
     s += len;
+    slot = 1;
     j += len;
     if (j == np) {
       j = 0;
@@ -439,33 +445,31 @@ static hipError_t stream_launch(const DecodeArgs &a, int64_t nw, hipStream_t str
 
 template <typename E, class F>
 static hipError_t parts_launch(const DecodeArgs &a, hipStream_t stream) {
-  static int per_cu = 0;  // resident workgroups per compute unit (cached)
-  if (per_cu == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_parts<E, F>, kBlock, 0) !=
-            hipSuccess ||
-        nb < 1)
-      nb = 1;
-    per_cu = nb;
-  }
-  const int64_t units = (int64_t)a.batch * a.bank.num_kv_heads * a.max_parts;
-  const int64_t blocks = std::min<int64_t>((int64_t)a.num_cus * per_cu, (units + kWaves - 1) / kWaves);
+  constexpr int G = F::kGroup;
+  const int64_t nw = a.nw;
+  const unsigned blocks = (unsigned)(nw / kWaves);
+  // The segment partials sit where the balanced split keeps its own.
+  const size_t slots = (size_t)nw * 2 * G;
+  float2 *part_ml = reinterpret_cast<float2 *>(a.part_m);
+  float *part_acc = reinterpret_cast<float *>(reinterpret_cast<char *>(a.part_m) +
+                                              (slots * 2 * sizeof(float) + 255) / 256 * 256);
   const size_t lds = sizeof(int) * ((size_t)a.batch + 1);
-  hipLaunchKernelGGL((decode_parts<E, F>), dim3((unsigned)blocks), dim3(kBlock), lds, stream,
+  hipLaunchKernelGGL((decode_parts<E, F>), dim3(blocks), dim3(kBlock), lds, stream,
                      static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                      a.bank.num_pages, a.bank.num_kv_heads,
                      static_cast<const typename E::storage *>(a.q), a.num_q_heads, a.page_table,
                      a.pt_stride, a.seq_lens, a.batch, a.max_seq_len, a.scale * kLog2e,
                      a.partition, a.max_parts, static_cast<typename E::storage *>(a.out), a.lse,
-                     a.part_m, a.part_l, a.part_acc,
-                     static_cast<const typename E::storage *>(a.k_new),
+                     part_ml, part_acc, static_cast<const typename E::storage *>(a.k_new),
                      static_cast<const typename E::storage *>(a.v_new),
                      static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v), a.latest);
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return e;
-  return launch_reduce(a.bank.dtype, a.batch, a.num_q_heads, F::kHeadDim, a.seq_lens,
-                       a.max_seq_len, a.partition, a.max_parts, a.part_m, a.part_l, a.part_acc,
-                       a.out, a.lse, true, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_parts_combine<E, G>), dim3(a.batch * a.bank.num_kv_heads),
+                     dim3(kBlock), 0, stream, a.bank.num_kv_heads, F::kHeadDim, a.seq_lens,
+                     a.batch, a.max_seq_len, a.partition, a.max_parts, nw, part_ml, part_acc,
+                     static_cast<typename E::storage *>(a.out), a.lse);
+  return hipGetLastError();
 }
 
 template <typename E, int D>
@@ -506,8 +510,8 @@ bool decode_parts_supported(const DecodeArgs &a) {
                                               : pages_per_step<BF16, 64>(g, latest))
                     : (a.bank.head_dim == 128 ? pages_per_step<F32, 128>(g, latest)
                                               : pages_per_step<F32, 64>(g, latest));
-  return a.max_parts > 1 && a.batch <= kPartsMaxBatch && s > 0 && a.partition % kPage == 0 &&
-         (a.partition / kPage) % s == 0;
+  return a.max_parts > 1 && a.nw >= kWaves && a.nw % kWaves == 0 && a.batch <= kPartsMaxBatch &&
+         s > 0 && a.partition % kPage == 0 && (a.partition / kPage) % s == 0;
 }
 
 hipError_t launch_decode_parts(const DecodeArgs &a, hipStream_t stream) {

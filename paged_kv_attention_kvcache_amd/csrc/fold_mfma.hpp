@@ -252,6 +252,18 @@ struct MfmaFold {
     st.l += __shfl_xor(st.l, 32);
   }
 
+  // Folds finished state p (after finish_wave) into `into`, as the combine of
+  // two partitions in order: each is rescaled to the larger max.
+  __device__ __forceinline__ static void merge(State &into, const State &p) {
+    const float mn = fmaxf(into.m, p.m);
+    const float ms = (mn == -INFINITY) ? 0.f : mn;
+    const float a = fast_exp2(into.m - ms), b = fast_exp2(p.m - ms);
+    into.l = into.l * a + p.l * b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) into.acc[j] = into.acc[j] * a + p.acc[j] * b;
+    into.m = mn;
+  }
+
   template <class Fn>
   __device__ __forceinline__ void emit(const State &st, Fn &&fn) const {
     if (n >= (PC ? ncols : G)) return;

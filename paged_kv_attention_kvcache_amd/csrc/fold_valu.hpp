@@ -236,6 +236,21 @@ struct ValuFold {
     }
   }
 
+  // Folds finished state p (after finish_wave) into `into`, as the combine of
+  // two partitions in order: each is rescaled to the larger max.
+  __device__ __forceinline__ static void merge(State &into, const State &p) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(into.m[g], p.m[g]);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      const float a = fast_exp2(into.m[g] - ms), b = fast_exp2(p.m[g] - ms);
+      into.l[g] = into.l[g] * a + p.l[g] * b;
+#pragma unroll
+      for (int e = 0; e < N; ++e) into.acc[g][e] = into.acc[g][e] * a + p.acc[g][e] * b;
+      into.m[g] = mn;
+    }
+  }
+
   template <class Fn>
   __device__ __forceinline__ void emit(const State &st, Fn &&fn) const {
     if (row != 0) return;

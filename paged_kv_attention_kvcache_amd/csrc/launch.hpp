@@ -46,6 +46,10 @@ struct DecodeArgs {
   // the same kernel. NULL: the pool already holds it.
   const void *k_new = nullptr, *v_new = nullptr;
   int32_t num_cus = 256;  // compute units of the device (sizes persistent grids)
+  // Waves of decode_parts' grid (a multiple of 4; 0: that kernel is not
+  // used). The workspace then also holds 2 * nw * G segment partials
+  // ((m, l) pairs, then acc at the next 256-byte boundary).
+  int64_t nw = 0;
   LatestArgs latest{};    // early-exit decode when latest.depth != null
 };
 
@@ -56,8 +60,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeArgs &a, int64_t nw, hipStream_t stream);
 // Waves of the stream kernel that fit on num_cus compute units at once.
 int stream_waves(int dtype, int head_dim, int group, int num_cus);
-// Fixed partitions streamed by a persistent grid (one wave per partition,
-// then decode_reduce); launch_decode takes it whenever it applies.
+// Fixed partitions streamed by a persistent grid (each partition folded by
+// one wave and combined in order in its registers), then the combine of
+// (request, kv head)s split between waves; launch_decode takes it whenever
+// it applies.
 constexpr int kPartsMaxBatch = 4096;  // rows whose prefix the kernel keeps in LDS
 bool decode_parts_supported(const DecodeArgs &a);
 hipError_t launch_decode_parts(const DecodeArgs &a, hipStream_t stream);

@@ -136,6 +136,15 @@ int64_t stream_wave_count(const pkv_pool *p, int32_t batch, int32_t hq, int32_t 
 }
 
 // Tokens per workgroup in the fixed and whole modes.
+// Waves of the streamed fixed-partition grid: as for the balanced split, and
+// no more than the call's partitions (rounded up to whole workgroups).
+int64_t parts_wave_count(const pkv_pool *p, int32_t batch, int32_t hq, int32_t max_seq_len,
+                         int64_t max_parts) {
+  const int64_t parts = (int64_t)batch * p->num_kv_heads * max_parts;
+  return std::max<int64_t>(4, std::min(stream_wave_count(p, batch, hq, max_seq_len),
+                                       (parts + 3) / 4 * 4));
+}
+
 int32_t fixed_partition(Mode m, int32_t max_seq_len, int32_t partition) {
   if (m == Mode::kWhole) return max_seq_len <= 16 ? 16 : (max_seq_len + 15) / 16 * 16;
   return partition > 0 ? partition : kDefaultPartition;
@@ -201,16 +210,23 @@ size_t paged_decode_workspace_bytes(const pkv_pool *pool, int32_t batch, int32_t
       partition < 0)
     return 0;
   const size_t D = (size_t)pool->head_dim;
+  const size_t G = (size_t)(num_q_heads / pool->num_kv_heads);
   const Mode mode = decode_mode(batch, pool->num_kv_heads, max_seq_len, partition);
-  if (mode == Mode::kStream) {
-    const size_t slots = (size_t)stream_wave_count(pool, batch, num_q_heads, max_seq_len) * 2 *
-                         (num_q_heads / pool->num_kv_heads);
+  // Segment partials: two (m, l, acc) slots per wave and head of the group.
+  auto seg = [&](int64_t nw) {
+    const size_t slots = (size_t)nw * 2 * G;
     return align_up(slots * 2 * sizeof(float)) + align_up(slots * D * sizeof(float));
-  }
+  };
+  if (mode == Mode::kStream) return seg(stream_wave_count(pool, batch, num_q_heads, max_seq_len));
   partition = fixed_partition(mode, max_seq_len, partition);
   const size_t parts = max_seq_len > 0 ? (size_t)(max_seq_len + partition - 1) / partition : 1;
   const size_t rows = (size_t)batch * num_q_heads;
-  return 2 * align_up(rows * parts * sizeof(float)) + align_up(rows * parts * D * sizeof(float));
+  const size_t fixed =
+      2 * align_up(rows * parts * sizeof(float)) + align_up(rows * parts * D * sizeof(float));
+  if (mode != Mode::kFixed) return fixed;
+  // the streamed kernel's segment partials share the space
+  return std::max(fixed, seg(parts_wave_count(pool, batch, num_q_heads, max_seq_len,
+                                              (int64_t)parts)));
 }
 
 namespace {
@@ -275,6 +291,8 @@ int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const 
   }
   const size_t rows = (size_t)batch * num_q_heads;
   const size_t ml = align_up(rows * max_parts * sizeof(float));
+  if (mode == Mode::kFixed)
+    a.nw = parts_wave_count(pool, batch, num_q_heads, max_seq_len, max_parts);
   a.part_m = reinterpret_cast<float *>(ws);
   a.part_l = reinterpret_cast<float *>(ws + ml);
   a.part_acc = reinterpret_cast<float *>(ws + 2 * ml);

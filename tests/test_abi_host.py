@@ -74,12 +74,16 @@ def test_bank_map_rejects(L):
 
 def test_workspace_bytes(L):
     # fixed partitions: rows * parts floats for m and l, rows * parts * D for
-    # acc, each 256-aligned
+    # acc, each 256-aligned; or, if larger, the streamed kernel's segment
+    # partials: two (m, l, acc) slots per wave and head of the group, for a
+    # grid of at most the call's 3 * 2 * 4 = 24 partitions (24 waves)
     st, keep = _pool(kv=2)
-    rows, parts, D = 3 * 8, 4, 128
+    rows, parts, D, G = 3 * 8, 4, 128, 4
     need = L.paged_decode_workspace_bytes(ctypes.byref(st), 3, 8, 2048, 512)
     al = lambda x: (x + 255) // 256 * 256
-    assert need == 2 * al(rows * parts * 4) + al(rows * parts * D * 4)
+    slots = 24 * 2 * G
+    assert need == max(2 * al(rows * parts * 4) + al(rows * parts * D * 4),
+                       al(slots * 2 * 4) + al(slots * D * 4))
     # balanced split: two (m, l, acc) slots per wave and head of the group
     assert L.paged_decode_workspace_bytes(ctypes.byref(st), 3, 8, 2048, 0) > 0
     assert L.paged_decode_workspace_bytes(ctypes.byref(st), 0, 8, 2048, 512) == 0
