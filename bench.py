@@ -67,7 +67,7 @@ class DecodeWorkload:
         import paged_kv_attention_kvcache_amd as pkv
         from paged_kv_attention_kvcache_amd import synth
 
-        self.name, self.hq, self.hkv, self.D = name, hq, hkv, D
+        self.name, self.hq, self.hkv, self.D, self.batch = name, hq, hkv, D, batch
         self.partition = partition  # 0: the library's balanced split
         rng = np.random.default_rng(seed)
         if alias > 0:
@@ -115,7 +115,6 @@ class DecodeWorkload:
         uniq_pages = len(np.unique(np.concatenate(
             [self.table[r, :-(-int(n) // 16)] for r, n in enumerate(self.seq)])))
         self.unique_bytes_per_call = uniq_pages * 2 * hkv * 16 * D * 2
-        self.batch = batch
         torch.cuda.synchronize()
         # Host copies for the CPU baseline, taken before any library kernel runs.
         self.snap = []

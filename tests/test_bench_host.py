@@ -36,3 +36,16 @@ def test_workload_configs_name_the_shapes():
     for name in ("ouro", "huginn", "longctx"):
         cfg = bench.CONFIG_TEXT[name]
         assert cfg["workload"] and cfg["page_size"] == 16 and cfg["head_dim"] == 128
+
+
+def test_kernel_labels_follow_the_split():
+    # the label bench.py reports for each split, from an object holding only
+    # the sizes kernel_for reads (no pool, no GPU)
+    wl = bench.DecodeWorkload.__new__(bench.DecodeWorkload)
+    wl.hq, wl.hkv, wl.D, wl.batch, wl.max_seq = 64, 8, 128, 256, 32768
+    assert wl.kernel_for("balanced", 0).startswith("decode_stream<BF16, MfmaFold<8>>")
+    assert wl.kernel_for("fixed", 512).startswith("decode_parts<BF16, MfmaFold<8>>")
+    assert wl.kernel_for("fixed", 48).startswith("decode_block<BF16, MfmaFold<8>>")
+    wl.hq = 16
+    assert wl.kernel_for("fixed", 48).startswith("decode_parts<BF16, ValuFold<BF16, 128, 2>>")
+    assert wl.kernel_for("whole", 0).startswith("decode_whole<")
