@@ -42,11 +42,15 @@ __device__ __forceinline__ void combine_row(const float *__restrict__ part_m,
                                             float &L, float &A) {
   const float *pm = part_m + rowh * max_parts;
   const float *pl = part_l + rowh * max_parts;
+  // Unrolled so that several partitions' loads are in flight at once (the
+  // fold order, and so the result, is unchanged).
   M = -INFINITY;
+#pragma unroll 8
   for (int j = 0; j < np; ++j) M = fmaxf(M, pm[j]);
   const float ms = (M == -INFINITY) ? 0.f : M;
   L = 0.f;
   A = 0.f;
+#pragma unroll 8
   for (int j = 0; j < np; ++j) {
     const float f = fast_exp2(pm[j] - ms);
     L = fmaf(pl[j], f, L);

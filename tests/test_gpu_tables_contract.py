@@ -38,8 +38,12 @@ def _bad_table(rng, batch, stride, num_pages):
     return t.astype(np.int32)
 
 
-@pytest.mark.parametrize("mode", ["whole", "balanced", "fixed"])
-def test_decode_tables_out_of_contract(mode):
+@pytest.mark.parametrize("mode,hq", [("whole", 16), ("balanced", 16), ("fixed", 16),
+                                     ("fixed", 64), ("fixed48", 64)])
+def test_decode_tables_out_of_contract(mode, hq):
+    # fixed with group 2 (vector fold) and group 8 (matrix-core fold) take the
+    # streamed fixed partitions; 48-token partitions with group 8 take one
+    # workgroup per partition
     import torch
 
     rng = np.random.default_rng(41)
@@ -51,15 +55,15 @@ def test_decode_tables_out_of_contract(mode):
     seq = rng.integers(-(1 << 30), 1 << 30, size=batch).astype(np.int32)
     seq[::4] = rng.integers(0, max_seq + 1, size=seq[::4].shape)
     table = _bad_table(rng, batch, stride, layout.num_pages)
-    q = to_dev(synth.draw(rng, (batch, 16, 128), "bf16"), "bf16")
-    partition = 64 if mode == "fixed" else 0
-    say(f"decode out-of-contract tables, {mode}: "
-        f"{pkv.split_mode(pool, batch, 16, max_seq, partition)}")
+    q = to_dev(synth.draw(rng, (batch, hq, 128), "bf16"), "bf16")
+    partition = {"fixed": 64, "fixed48": 48}.get(mode, 0)
+    say(f"decode out-of-contract tables, {mode} hq={hq}: "
+        f"{pkv.split_mode(pool, batch, hq, max_seq, partition)}")
     out, lse = pkv.decode(pool, 0, 0, q, i32_dev(table), i32_dev(seq), max_seq,
                           partition=partition)
     torch.cuda.synchronize()
     assert np.array_equal(bits(pool.k), before[0]) and np.array_equal(bits(pool.v), before[1])
-    assert out.shape == (batch, 16, 128) and lse.shape == (batch, 16)
+    assert out.shape == (batch, hq, 128) and lse.shape == (batch, hq)
 
 
 @pytest.mark.parametrize("dtype,D,max_q", [("bf16", 128, 256), ("f32", 64, 256),
