@@ -296,7 +296,13 @@ int paged_decode_reduce(int32_t dtype, int32_t batch, int32_t num_q_heads,
  *   cu_q_lens:  DEVICE int32 [batch + 1], cu_q_lens[0] = 0, cu_q_lens[batch] = total_q
  *   page_table, seq_lens: as for decode
  *   max_q_len, max_seq_len: HOST bounds on q_len and n
- *   out:        DEVICE [total_q][num_q_heads][head_dim]; lse fp32 [total_q][num_q_heads] or NULL */
+ *   out:        DEVICE [total_q][num_q_heads][head_dim]; lse fp32 [total_q][num_q_heads] or NULL
+ * max_q_len also picks the kernel: with bf16 and head_dim 128, a call whose
+ * max_q_len times the GQA group is at most 16 runs as one decode-style pass
+ * per (request, kv head) (all its rows share one 16-column matrix-core
+ * operand); longer chunks take 128-row query tiles on matrix cores. A q_len
+ * above max_q_len is outside the contract (unspecified rows, no access
+ * outside the buffers). */
 int paged_prefill_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                        const void *q, int32_t num_q_heads,
                        const int32_t *cu_q_lens, int32_t total_q,
