@@ -59,7 +59,9 @@ Mode decode_mode(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t partit
   if (partition > 0) return Mode::kFixed;
   if (max_seq_len <= kWholeShortSeq) return Mode::kWhole;
   if (max_seq_len <= kWholeMaxSeq && (int64_t)batch * hkv >= kWholeMinPairs) return Mode::kWhole;
-  return batch <= kStreamMaxBatch ? Mode::kStream : Mode::kFixed;
+  // the balanced split indexes the call's pages with 32-bit prefix sums
+  const int64_t pages = (int64_t)batch * hkv * ((max_seq_len + 15) / 16);
+  return batch <= kStreamMaxBatch && pages <= INT32_MAX ? Mode::kStream : Mode::kFixed;
 }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -291,7 +293,8 @@ int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const 
   }
   const size_t rows = (size_t)batch * num_q_heads;
   const size_t ml = align_up(rows * max_parts * sizeof(float));
-  if (mode == Mode::kFixed)
+  // streamed fixed partitions index the call's partitions with 32-bit sums
+  if (mode == Mode::kFixed && (int64_t)batch * pool->num_kv_heads * max_parts <= INT32_MAX)
     a.nw = parts_wave_count(pool, batch, num_q_heads, max_seq_len, max_parts);
   a.part_m = reinterpret_cast<float *>(ws);
   a.part_l = reinterpret_cast<float *>(ws + ml);

@@ -90,6 +90,18 @@ def test_workspace_bytes(L):
     assert L.paged_decode_workspace_bytes(ctypes.byref(st), 3, 7, 2048, 512) == 0
 
 
+def test_split_mode_keeps_prefix_sums_in_32_bits(L):
+    # the balanced split sums the call's pages in 32 bits: a call with more
+    # than 2^31 - 1 (request, kv head, page) entries takes fixed partitions
+    st, keep = _pool(kv=8)
+    mode = lambda b, s, p=0: L.paged_decode_split_mode(ctypes.byref(st), b, 64, s, p)
+    assert mode(256, 32768) == 1                    # balanced
+    assert mode(4096, (1 << 20) - 16) == 1          # 4096 * 8 * 65535 pages fit
+    assert mode(4096, 1 << 20) == 2                 # 4096 * 8 * 65536 = 2^31 do not
+    assert mode(4097, 32768) == 2                   # more rows than the split keeps
+    assert mode(64, 2048) == 0                      # whole contexts
+
+
 def _pool(dtype=1, page_size=16, head_dim=128, planes=2, layers=3, rec=(0, 3), kv=2,
           pages=8, ptr=1 << 20):
     bank_of, nb = pkv.bank_map(planes, layers, *rec)
