@@ -41,7 +41,7 @@ def say(*a):
 # ------------------------------------------------------------------ store_kv
 
 WRITE_CASES = {
-    # config 1 shape: fp32, 64-page pool, 2 KV heads, head_dim 64
+    # tiny decode shape: fp32, 64-page pool, 2 KV heads, head_dim 64
     "tiny_f32": dict(dtype="f32", batch=4, seq_range=(17, 64), num_q_heads=4, num_kv_heads=2,
                      head_dim=64, num_pages=64),
     # Ouro shape (fewer requests): bf16, 8 KV heads, head_dim 128, 4 planes x 3 layers
@@ -93,7 +93,7 @@ def test_kv_write_overwrite_and_padding():
 
 
 def test_kv_write_prefill_chunks_bit_exact():
-    # config 4 writes: 8 prompts x 512 tokens in chunks of 128, 32 heads, D 128
+    # cached-prefix prefill writes: 8 prompts x 512 tokens in chunks of 128, 32 heads, D 128
     case = synth.make_prefill_case(1, "bf16", [512] * 8, 32, 32, 128)
     gp, op = gpu_pool(case.layout), oracle_pool(case.layout)
     for ch in synth.chunk_schedule(case, 128):
@@ -108,17 +108,17 @@ def test_kv_write_prefill_chunks_bit_exact():
 # ------------------------------------------------------------------ decode
 
 DECODE_CASES = {
-    # config 1: tiny decode, fp32
-    "c1_tiny_f32": dict(dtype="f32", batch=4, seq_range=(17, 64), num_q_heads=4,
+    # tiny decode, fp32
+    "tiny_f32": dict(dtype="f32", batch=4, seq_range=(17, 64), num_q_heads=4,
                         num_kv_heads=2, head_dim=64, num_pages=64),
-    # config 2 shape (16 of the 64 requests): Ouro, G = 2
-    "c2_ouro": dict(dtype="bf16", batch=16, seq_range=(512, 2048), num_q_heads=16,
+    # Ouro shape (16 of the 64 requests), G = 2
+    "ouro": dict(dtype="bf16", batch=16, seq_range=(512, 2048), num_q_heads=16,
                     num_kv_heads=8, head_dim=128),
-    # config 3 shape: Huginn MHA with 78% aliased prompt pages
-    "c3_huginn": dict(dtype="bf16", batch=16, seq_range=(200, 2000), num_q_heads=32,
+    # Huginn shape: MHA with 78% aliased prompt pages
+    "huginn": dict(dtype="bf16", batch=16, seq_range=(200, 2000), num_q_heads=32,
                       num_kv_heads=32, head_dim=128, alias_frac=0.78),
-    # config 5 shape (4 of the 256 requests): GQA group 8, long context
-    "c5_longctx": dict(dtype="bf16", batch=4, seq_range=(8192, 32768), num_q_heads=64,
+    # long-context shape (4 of the 256 requests): GQA group 8, long context
+    "longctx": dict(dtype="bf16", batch=4, seq_range=(8192, 32768), num_q_heads=64,
                        num_kv_heads=8, head_dim=128),
     # other kernel instances: bf16 head_dim 64 group 4; fp32 head_dim 128 group 1
     "bf16_d64_g4": dict(dtype="bf16", batch=6, seq_range=(1, 700), num_q_heads=8,
@@ -153,7 +153,7 @@ def test_decode_parity(name, seed):
             check(f"{name}/s{seed}/q{q_scale}/p{partition}", case.layout.dtype, out, ro, rl, lse)
 
 
-APPEND_CASES = ["c1_tiny_f32", "c2_ouro", "c3_huginn", "c5_longctx", "bf16_d128_g4",
+APPEND_CASES = ["tiny_f32", "ouro", "huginn", "longctx", "bf16_d128_g4",
                 "bf16_d64_g4", "whole_g2", "whole_g8"]
 
 
@@ -284,10 +284,10 @@ def _prefill_compare(tag, case, chunks, gp, op):
 
 
 @pytest.mark.parametrize("mode", ["suffix", "chunk128", "chunk2048"])
-def test_prefill_config4(mode):
+def test_prefill_cached_prefix_workload(mode):
     # 8 prompts of 512 tokens, 32 MHA heads, head_dim 128, bf16; the first 496
     # tokens of each prompt are cached pages (suffix mode) or prompts are cold.
-    say(f"prefill config4 {mode}")
+    say(f"prefill cached-prefix workload {mode}")
     case = synth.make_prefill_case(0, "bf16", [512] * 8, 32, 32, 128)
     gp, op = gpu_pool(case.layout), oracle_pool(case.layout)
     if mode == "suffix":
@@ -297,7 +297,7 @@ def test_prefill_config4(mode):
         chunks = synth.chunk_schedule(case, 4096, start=[496] * 8)
     else:
         chunks = synth.chunk_schedule(case, 128 if mode == "chunk128" else 2048)
-    _prefill_compare(f"c4/{mode}", case, chunks, gp, op)
+    _prefill_compare(f"cached_prefix/{mode}", case, chunks, gp, op)
 
 
 def test_prefill_shared_prefix_suffix():
@@ -407,7 +407,7 @@ def test_prefill_long_context(lens, start):
 # ------------------------------------------------------------------ bitwise invariants
 
 def test_decode_bitwise_invariants():
-    kw = DECODE_CASES["c3_huginn"]
+    kw = DECODE_CASES["huginn"]
     case = synth.make_decode_case(4, **kw)
     a, la, pool = gpu_decode_case(case)
     # run to run
@@ -454,15 +454,15 @@ def test_prefill_bitwise_shared_vs_private():
 # ------------------------------------------------------------------ full-size, sampled
 
 FULL = {
-    # config 2: one bank call at the full Ouro shape
-    "c2_full": dict(B=64, lo=512, hi=2048, hq=16, hkv=8, alias=0.0, rows=[0, 31, 63]),
-    # config 3: Huginn, 78% aliased prompts
-    "c3_full": dict(B=16, lo=200, hi=2000, hq=32, hkv=32, alias=0.78, rows=[0, 7, 15]),
-    # config 5: 256 requests, 8k-32k context, GQA 8; the library's balanced
+    # one bank call at the full Ouro shape
+    "ouro_full": dict(B=64, lo=512, hi=2048, hq=16, hkv=8, alias=0.0, rows=[0, 31, 63]),
+    # Huginn, 78% aliased prompts
+    "huginn_full": dict(B=16, lo=200, hi=2000, hq=32, hkv=32, alias=0.78, rows=[0, 7, 15]),
+    # long context: 256 requests, 8k-32k context, GQA 8; the library's balanced
     # split and the stated split-K over fixed 512-token partitions
-    "c5_full": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255]),
-    "c5_full_p512": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255],
-                         partition=512),
+    "longctx_full": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255]),
+    "longctx_full_p512": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255],
+                              partition=512),
 }
 
 
