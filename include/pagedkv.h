@@ -375,6 +375,20 @@ int pkv_mgr_note_write(pkv_page_mgr *mgr, int32_t plane, int32_t layer, int32_t 
 int32_t pkv_mgr_published_prefix(const pkv_page_mgr *mgr, int32_t planes_used,
                                  const int32_t *page_ids, int32_t n_pages);
 
+/* The slots of a span of positions of each request ([FFM] "When scheduler
+ * does the work": position pos of a request lives in slot page_table[r][pos /
+ * page_size] * page_size + pos % page_size; [FFM] "LOTUS": a latent block's
+ * slots are handed out once and every pass writes the same ones). Host only:
+ * page_table [batch][stride], starts [batch] and slots [batch][span] are HOST
+ * arrays. For r < batch and j < span, with pos = starts[r] + j:
+ *   slots[r * span + j] = page_table[r * stride + pos / page_size] * page_size
+ *                         + pos % page_size.
+ * PKV_EINVAL, with nothing written, for a negative start, a span that runs
+ * past stride * page_size, or a page id of the span outside [0, num_pages). */
+int pkv_span_slots(const int32_t *page_table, int32_t stride, int32_t page_size,
+                   int32_t num_pages, const int32_t *starts, int32_t batch, int32_t span,
+                   int32_t *slots);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *pkv_last_error(void);
 

@@ -57,7 +57,8 @@ EXPORTS = ("pkv_bank_map", "pkv_pool_bytes", "paged_kv_write", "paged_decode_wor
            "paged_decode_step_graph_destroy", "paged_decode_reduce", "paged_prefill_attn",
            "paged_extend_attn", "pkv_mgr_create", "pkv_mgr_destroy", "pkv_mgr_free_count",
            "pkv_mgr_alloc", "pkv_mgr_retain", "pkv_mgr_release", "pkv_mgr_refcount",
-           "pkv_mgr_note_write", "pkv_mgr_published_prefix", "pkv_last_error")
+           "pkv_mgr_note_write", "pkv_mgr_published_prefix", "pkv_span_slots",
+           "pkv_last_error")
 
 
 def lib():
@@ -120,6 +121,8 @@ def lib():
         L.pkv_mgr_note_write.restype = ctypes.c_int
         L.pkv_mgr_published_prefix.argtypes = [P, i32, P, i32]
         L.pkv_mgr_published_prefix.restype = i32
+        L.pkv_span_slots.argtypes = [P, i32, i32, i32, P, i32, i32, P]
+        L.pkv_span_slots.restype = ctypes.c_int
         L.pkv_last_error.argtypes = []
         L.pkv_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -436,7 +439,8 @@ class LotusBlock:
     request's block of positions [start_r, start_r + block) is handed the
     same slots on every pass, so pass k overwrites pass k-1's K/V and attends
     the prefix plus its own block ("Faster fuzzy minds", section "LOTUS").
-    The slots are computed once, from the page table, when the loop starts.
+    The slots are computed once by the library (pkv_span_slots), from the
+    page table, when the loop starts.
 
     pass_(k, v, q) runs one pass: k, v [B * block, Hkv, D] and q
     [B * block, Hq, D], request-major."""
@@ -444,16 +448,19 @@ class LotusBlock:
     def __init__(self, pool: Pool, plane: int, layer: int, page_table, starts, block: int,
                  page_size: int = 16):
         torch = _torch()
-        starts = np.asarray(starts, np.int64)
+        starts = np.ascontiguousarray(starts, dtype=np.int32)
         table = page_table.cpu().numpy() if hasattr(page_table, "cpu") else np.asarray(page_table)
+        table = np.ascontiguousarray(table, dtype=np.int32)
         B = len(starts)
-        pos = starts[:, None] + np.arange(block)[None, :]
-        slots = table[np.arange(B)[:, None], pos // page_size] * page_size + pos % page_size
+        slots = np.empty((B, block), np.int32)
+        _check(lib().pkv_span_slots(table.ctypes.data, table.shape[1], page_size,
+                                    pool.num_pages, starts.ctypes.data, B, block,
+                                    slots.ctypes.data))
         dev = pool.k.device
         self.pool, self.plane, self.layer, self.block = pool, plane, layer, block
         self.page_table = page_table if hasattr(page_table, "data_ptr") else \
-            torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to(dev)
-        self.slots = torch.from_numpy(slots.reshape(-1).astype(np.int32)).to(dev)
+            torch.from_numpy(table).to(dev)
+        self.slots = torch.from_numpy(slots.reshape(-1)).to(dev)
         self.cu = torch.from_numpy((np.arange(B + 1) * block).astype(np.int32)).to(dev)
         ends = (starts + block).astype(np.int32)
         self.seq = torch.from_numpy(ends).to(dev)

@@ -12,6 +12,7 @@
 // partition are finished directly by the partial kernel, and the combine
 // kernel is launched only when some row can span several partitions.
 #include <algorithm>
+#include <atomic>
 
 #include "folds.hpp"
 #include "launch.hpp"
@@ -226,8 +227,12 @@ static hipError_t decode_fold(const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid(a.max_parts, a.bank.num_kv_heads, a.batch);
   constexpr int W = decode_waves<F>();
   if (a.max_parts == 1 && a.batch <= kWholeMaxBatch) {
-    // As many persistent workgroups as are resident at once (cached).
-    static int per_cu = 0;
+    // As many persistent workgroups as are resident at once. The occupancy
+    // is a property of the kernel binary, which is built for gfx950 alone,
+    // so one cached value serves every device; host threads that race to
+    // fill it store the same value.
+    static std::atomic<int> cached{0};
+    int per_cu = cached.load(std::memory_order_relaxed);
     if (per_cu == 0) {
       int nb = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_whole<E, F, W>, 64 * W, 0) !=
@@ -235,6 +240,7 @@ static hipError_t decode_fold(const DecodeArgs &a, hipStream_t stream) {
           nb < 1)
         nb = 1;
       per_cu = nb;
+      cached.store(nb, std::memory_order_relaxed);
     }
     const int units = a.batch * a.bank.num_kv_heads;
     const int blocks = std::min(units, a.num_cus * per_cu);

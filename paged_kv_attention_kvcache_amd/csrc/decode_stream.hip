@@ -14,6 +14,7 @@
 // grid size, so results are bitwise repeatable and independent of where the
 // pages live.
 #include <algorithm>
+#include <atomic>
 
 #include "folds.hpp"
 #include "launch.hpp"
@@ -410,13 +411,19 @@ static int blocks_by_group(int g) {
 }
 
 int stream_waves(int dtype, int head_dim, int group, int num_cus) {
-  static int cache[2][2][9] = {};  // [dtype][head_dim 64/128][group]: blocks per CU
-  int &bpc = cache[dtype == 1][head_dim == 128][group & 7 ? group : 8];
-  if (bpc == 0)
+  // [dtype][head_dim 64/128][group]: blocks per CU. Occupancy is a property
+  // of the kernel binary (gfx950 only), the same on every device; host
+  // threads that race to fill an entry store the same value.
+  static std::atomic<int> cache[2][2][9];
+  std::atomic<int> &slot = cache[dtype == 1][head_dim == 128][group & 7 ? group : 8];
+  int bpc = slot.load(std::memory_order_relaxed);
+  if (bpc == 0) {
     bpc = dtype == 1 ? (head_dim == 128 ? blocks_by_group<BF16, 128>(group)
                                         : blocks_by_group<BF16, 64>(group))
                      : (head_dim == 128 ? blocks_by_group<F32, 128>(group)
                                         : blocks_by_group<F32, 64>(group));
+    slot.store(bpc, std::memory_order_relaxed);
+  }
   return num_cus * bpc * kWaves;
 }
 

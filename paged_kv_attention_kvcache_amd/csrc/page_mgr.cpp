@@ -197,4 +197,31 @@ int32_t pkv_mgr_published_prefix(const pkv_page_mgr *m, int32_t planes_used,
   return k;
 }
 
+int pkv_span_slots(const int32_t *page_table, int32_t stride, int32_t page_size,
+                   int32_t num_pages, const int32_t *starts, int32_t batch, int32_t span,
+                   int32_t *slots) {
+  if (!page_table || !starts || !slots || stride <= 0 || page_size <= 0 || num_pages <= 0 ||
+      batch < 0 || span < 0)
+    return mfail(PKV_EINVAL, "pkv_span_slots: bad arguments");
+  if ((int64_t)num_pages * page_size > INT32_MAX)
+    return mfail(PKV_EINVAL, "pkv_span_slots: slots of this pool overflow int32");
+  // Check everything first: nothing is written on failure.
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t lo = starts[r], hi = lo + span;
+    if (lo < 0 || (span > 0 && hi > (int64_t)stride * page_size))
+      return mfail(PKV_EINVAL, "pkv_span_slots: span outside the page-table row");
+    for (int64_t p = lo; p < hi; p += page_size - p % page_size) {
+      const int32_t id = page_table[(size_t)r * stride + p / page_size];
+      if (id < 0 || id >= num_pages) return mfail(PKV_EINVAL, "pkv_span_slots: bad page id");
+    }
+  }
+  for (int32_t r = 0; r < batch; ++r)
+    for (int32_t j = 0; j < span; ++j) {
+      const int64_t p = (int64_t)starts[r] + j;
+      slots[(size_t)r * span + j] =
+          page_table[(size_t)r * stride + p / page_size] * page_size + (int32_t)(p % page_size);
+    }
+  return pkv::set_error(PKV_OK, "");
+}
+
 }  // extern "C"

@@ -346,6 +346,8 @@ int paged_decode_step(const pkv_pool *pool, int32_t num_calls, const int32_t *pl
     int rc = resolve_bank(pool, plane_ids[i], layer_ids[i], &bank);
     if (rc) return fail_call(rc, i);
     if (!q[i] || !out[i]) return fail(PKV_EINVAL, "call %d: q / out is NULL", i);
+    if ((reinterpret_cast<uintptr_t>(q[i]) | reinterpret_cast<uintptr_t>(out[i])) & 15)
+      return fail(PKV_EINVAL, "call %d: q and out must be 16-byte aligned", i);
     if (k_new && (!k_new[i] || !v_new[i]))
       return fail(PKV_EINVAL, "call %d: k_new / v_new is NULL", i);
     if (k_new && ((reinterpret_cast<uintptr_t>(k_new[i]) | reinterpret_cast<uintptr_t>(v_new[i])) & 15))

@@ -203,6 +203,19 @@ def test_decode_step_validation(L):
     assert step([0], [0], kv="k") == pkv.PKV_EINVAL      # k_new without v_new
     assert step([0], [0], n=-1) == pkv.PKV_EINVAL
     assert step([], [], n=0) == pkv.PKV_OK               # nothing to do
+    # a misaligned q or out in call 1 rejects the step before call 0 is
+    # enqueued (with no GPU here, enqueueing call 0 would report a launch
+    # failure instead)
+    for which in ("q", "out"):
+        pl = (ctypes.c_int32 * 2)(0, 0)
+        ly = (ctypes.c_int32 * 2)(0, 1)
+        good = (P * 2)(FAKE, FAKE)
+        bad = (P * 2)(FAKE, FAKE + 8)
+        qp, op = (bad, good) if which == "q" else (good, bad)
+        rc = L.paged_decode_step(ctypes.byref(st), 2, pl, ly, good, good, qp, 4, FAKE, 4, FAKE,
+                                 2, 64, 1.0, 0, op, None, FAKE, 1 << 30, None)
+        assert rc == pkv.PKV_EINVAL, which
+        assert "call 1" in pkv.last_error() and "aligned" in pkv.last_error()
     handle = ctypes.c_void_p()
     pl = (ctypes.c_int32 * 1)(0)
     ptrs = (P * 1)(FAKE)
@@ -227,3 +240,36 @@ def test_decode_latest_validation(L):
     assert call(hq=8) == pkv.PKV_EUNSUPPORTED           # group 4
     assert call(layer=0, plane=1) == pkv.PKV_ENOTHELD   # plane 1 does not hold layer 0
     assert call(layer=0, plane=0, max_seq=65) == pkv.PKV_EINVAL  # beyond stride * page_size
+
+
+def test_span_slots(L):
+    # pkv_span_slots against the slot definition written out position by
+    # position: page id of the position's page times 16, plus its offset
+    rng = np.random.default_rng(3)
+    B, stride, pages = 5, 9, 64
+    table = rng.permutation(pages)[:B * stride].reshape(B, stride).astype(np.int32)
+    starts = np.array([0, 5, 16, 31, 80], np.int32)
+    span = 64
+    out = np.full((B, span), -9, np.int32)
+    args = lambda st, sp, o: (table.ctypes.data, stride, 16, pages, st.ctypes.data, B, sp,
+                              o.ctypes.data)
+    assert L.pkv_span_slots(*args(starts, span, out)) == pkv.PKV_OK
+    for r in range(B):
+        for j in range(span):
+            pos = int(starts[r]) + j
+            assert out[r, j] == table[r, pos // 16] * 16 + pos % 16
+    # errors write nothing
+    for bad_starts, bad_span in ((np.array([0, 5, 16, 31, 81], np.int32), span),
+                                 (np.array([-1, 0, 0, 0, 0], np.int32), 4)):
+        o = np.full((B, bad_span), -9, np.int32)
+        assert L.pkv_span_slots(*args(bad_starts, bad_span, o)) == pkv.PKV_EINVAL
+        assert (o == -9).all()
+    t2 = table.copy()
+    t2[4, 8] = pages  # a page id outside the pool, inside the span of request 4
+    o = np.full((B, span), -9, np.int32)
+    assert L.pkv_span_slots(t2.ctypes.data, stride, 16, pages, starts.ctypes.data, B, span,
+                            o.ctypes.data) == pkv.PKV_EINVAL
+    assert (o == -9).all()
+    # the binding's LotusBlock takes its slots from the library
+    assert "pkv_span_slots" in open(os.path.join(ROOT, "paged_kv_attention_kvcache_amd",
+                                                 "__init__.py")).read()
