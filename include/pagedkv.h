@@ -28,7 +28,8 @@
  * Conventions for every entry point:
  *   - Ownership: the caller owns every buffer. The library allocates no
  *     device memory and keeps no state between calls except a thread-local
- *     error string.
+ *     error string (and, for paged_decode_attn_noalloc, one fixed scratch
+ *     array per GPU, placed when its code is loaded).
  *   - Asynchrony: device work is enqueued on `stream` (a hipStream_t passed
  *     as void*; NULL = the null stream) and the call returns without
  *     synchronising. Buffers must stay valid until the stream reaches the
@@ -167,6 +168,27 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                       int32_t max_seq_len, float scale, int32_t partition,
                       void *out, float *lse, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* paged_decode_attn for callers that cannot allocate device memory: code
+ * under HIP stream capture, tight serving loops, harnesses that forbid
+ * allocation. It takes no workspace; the split-K partials go to a
+ * library-held device array of PKV_SCRATCH_BYTES on each GPU (placed when
+ * the library's code is loaded on that GPU, held until the process ends).
+ * The call allocates nothing. Every other argument, the results and the
+ * errors are those of paged_decode_attn, and the results are bitwise equal
+ * to paged_decode_attn's with a workspace of its own. Sizes whose
+ * paged_decode_workspace_bytes exceeds PKV_SCRATCH_BYTES return
+ * PKV_EWORKSPACE with nothing enqueued (e.g. many long contexts on small
+ * fixed partitions). All calls on one GPU share its array, which keeps the
+ * last call's contents: calls that overlap on one GPU (other streams, other
+ * host threads) race and give unspecified results; calls on one stream are
+ * ordered and safe. */
+#define PKV_SCRATCH_BYTES (32 << 20)
+int paged_decode_attn_noalloc(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                              const void *q, int32_t num_q_heads, const int32_t *page_table,
+                              int32_t page_table_stride, const int32_t *seq_lens,
+                              int32_t batch, int32_t max_seq_len, float scale,
+                              int32_t partition, void *out, float *lse, void *stream);
 
 /* Which split paged_decode_attn takes for these sizes: 0 = whole contexts
  * (one workgroup per request and kv head), 1 = balanced split + combine,

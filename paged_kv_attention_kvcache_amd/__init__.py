@@ -24,6 +24,7 @@ PKV_F32, PKV_BF16 = 0, 1
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_ENOTHELD, PKV_EWORKSPACE, PKV_ELAUNCH = 0, -1, -2, -3, -4, -5
 PKV_ENOSPACE = -6
 DEFAULT_PARTITION = 512
+SCRATCH_BYTES = 32 << 20  # PKV_SCRATCH_BYTES: paged_decode_attn_noalloc's per-GPU array
 
 _lib = None
 
@@ -51,7 +52,8 @@ class _Pool(ctypes.Structure):
 
 
 EXPORTS = ("pkv_bank_map", "pkv_pool_bytes", "paged_kv_write", "paged_decode_workspace_bytes",
-           "paged_decode_attn", "paged_decode_append_attn", "paged_decode_latest_attn",
+           "paged_decode_attn", "paged_decode_attn_noalloc", "paged_decode_append_attn",
+           "paged_decode_latest_attn",
            "paged_decode_split_mode",
            "paged_decode_step", "paged_decode_step_capture", "paged_decode_step_graph_launch",
            "paged_decode_step_graph_destroy", "paged_decode_reduce", "paged_prefill_attn",
@@ -80,6 +82,9 @@ def lib():
         L.paged_decode_attn.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, i32, ctypes.c_float,
                                         i32, P, P, P, sz, P]
         L.paged_decode_attn.restype = ctypes.c_int
+        L.paged_decode_attn_noalloc.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, i32,
+                                                ctypes.c_float, i32, P, P, P]
+        L.paged_decode_attn_noalloc.restype = ctypes.c_int
         L.paged_decode_append_attn.argtypes = [P, i32, i32, P, P, P, i32, P, i32, P, i32, i32,
                                                ctypes.c_float, i32, P, P, P, sz, P]
         L.paged_decode_append_attn.restype = ctypes.c_int
@@ -255,6 +260,23 @@ def decode(pool: Pool, plane: int, layer: int, q, page_table, seq_lens, max_seq_
                                    int(page_table.shape[1]), _dptr(seq_lens), B, max_seq_len,
                                    float(scale), partition, _dptr(out), _dptr(lse),
                                    _dptr(workspace), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def decode_noalloc(pool: Pool, plane: int, layer: int, q, page_table, seq_lens,
+                   max_seq_len: int, out, lse=None, scale: float | None = None,
+                   partition: int = 0, stream=None):
+    """paged_decode_attn_noalloc: decode attention whose split-K partials go
+    to the library's fixed per-GPU scratch array, so nothing is allocated
+    here or in the library. out [B, Hq, D] and lse [B, Hq] (or None) are the
+    caller's. Returns (out, lse)."""
+    B, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(lib().paged_decode_attn_noalloc(pool.ref, plane, layer, _dptr(q), Hq,
+                                           _dptr(page_table), int(page_table.shape[1]),
+                                           _dptr(seq_lens), B, max_seq_len, float(scale),
+                                           partition, _dptr(out), _dptr(lse), _stream(stream)))
     return out, lse
 
 

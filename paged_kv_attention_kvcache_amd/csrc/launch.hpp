@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "common.hpp"
+#include "pagedkv.h"
 
 namespace pkv {
 
@@ -100,5 +101,15 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
 // 16-column decode-style pass per (request, kv head); launch_prefill picks it first.
 bool prefill_cols_supported(const PrefillArgs &a);
 hipError_t launch_prefill_cols(const PrefillArgs &a, hipStream_t stream);
+
+// paged_decode_attn with its split-K workspace supplied by `scratch` (which
+// stores a device pointer of scratch_bytes bytes and returns 0, or returns a
+// negative code), called only after every argument has been validated and
+// the sizes found to fit in scratch_bytes.
+int decode_scratch(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
+                   const void *q, int32_t num_q_heads, const int32_t *page_table,
+                   int32_t page_table_stride, const int32_t *seq_lens, int32_t batch,
+                   int32_t max_seq_len, float scale, int32_t partition, void *out, float *lse,
+                   int (*scratch)(void **), size_t scratch_bytes, void *stream);
 
 }  // namespace pkv

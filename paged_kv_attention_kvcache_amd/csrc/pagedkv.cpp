@@ -238,7 +238,8 @@ int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const 
                 const int32_t *page_table, int32_t page_table_stride, const int32_t *seq_lens,
                 int32_t batch, int32_t max_seq_len, float scale, int32_t partition, void *out,
                 float *lse, void *workspace, size_t workspace_bytes, void *stream,
-                const pkv::LatestArgs *latest = nullptr) {
+                const pkv::LatestArgs *latest = nullptr,
+                int (*scratch)(void **) = nullptr) {
   pkv::Bank bank;
   int rc = resolve_bank(pool, plane_id, layer_id, &bank);
   if (rc) return rc;
@@ -255,6 +256,16 @@ int decode_impl(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const 
     return fail(PKV_EINVAL, "partition %d must be 0 or a positive multiple of 16", partition);
   const size_t need = paged_decode_workspace_bytes(pool, batch, num_q_heads, max_seq_len,
                                                    partition);
+  if (scratch) {
+    // The library's own scratch array: bounded, looked up only once every
+    // argument has been validated.
+    if (workspace_bytes < need)
+      return fail(PKV_EWORKSPACE,
+                  "these sizes need %zu bytes of split-K scratch, more than the library's %zu "
+                  "(use paged_decode_attn with a workspace)",
+                  need, workspace_bytes);
+    if ((rc = scratch(&workspace))) return rc;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
   const Mode mode = decode_mode(batch, pool->num_kv_heads, max_seq_len, partition);
@@ -313,6 +324,21 @@ int paged_decode_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, 
                      page_table_stride, seq_lens, batch, max_seq_len, scale, partition, out, lse,
                      workspace, workspace_bytes, stream);
 }
+
+}  // extern "C"
+
+int pkv::decode_scratch(const pkv_pool *pool, int32_t plane_id, int32_t layer_id, const void *q,
+                        int32_t num_q_heads, const int32_t *page_table,
+                        int32_t page_table_stride, const int32_t *seq_lens, int32_t batch,
+                        int32_t max_seq_len, float scale, int32_t partition, void *out,
+                        float *lse, int (*scratch)(void **), size_t scratch_bytes,
+                        void *stream) {
+  return decode_impl(pool, plane_id, layer_id, nullptr, nullptr, q, num_q_heads, page_table,
+                     page_table_stride, seq_lens, batch, max_seq_len, scale, partition, out, lse,
+                     nullptr, scratch_bytes, stream, nullptr, scratch);
+}
+
+extern "C" {
 
 int paged_decode_append_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                              const void *k_new, const void *v_new, const void *q,

@@ -273,3 +273,23 @@ def test_span_slots(L):
     # the binding's LotusBlock takes its slots from the library
     assert "pkv_span_slots" in open(os.path.join(ROOT, "paged_kv_attention_kvcache_amd",
                                                  "__init__.py")).read()
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(L):
+    # the header's PKV_SCRATCH_BYTES is the binding's constant
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_SCRATCH_BYTES \((\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pkv.SCRATCH_BYTES
+    # 256 long contexts on fixed 512-token partitions need far more than the
+    # scratch array: rejected, with nothing enqueued
+    st, keep = _pool(kv=8, pages=1 << 16)
+    call = lambda part, batch=256, max_seq=32768: L.paged_decode_attn_noalloc(
+        ctypes.byref(st), 0, 0, FAKE, 64, FAKE, 2048, FAKE, batch, max_seq, 1.0, part, FAKE,
+        None, None)
+    need = L.paged_decode_workspace_bytes(ctypes.byref(st), 256, 64, 32768, 512)
+    assert need > pkv.SCRATCH_BYTES
+    assert call(512) == pkv.PKV_EWORKSPACE
+    assert "scratch" in pkv.last_error()
+    # invalid sizes report paged_decode_attn's own errors
+    assert call(24) == pkv.PKV_EINVAL                   # partition not a multiple of 16
+    assert call(0, batch=0) == pkv.PKV_EINVAL
