@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "common.hpp"
+#include "args.hpp"
 #include "pagedkv.h"
 
 namespace pkv {

@@ -152,3 +152,32 @@ def sample_for_oracle(k_bank, v_bank, page_table: np.ndarray, seq_lens: np.ndarr
 def say(*a):
     """Names the case about to run (flushed, so a failing run shows it)."""
     print(*a, file=sys.stderr, flush=True)
+
+
+def full_size_pool(f, seed=11):
+    """The full workload's pool, page table, lengths and step inputs, generated
+    on the device as the benchmark does."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    if f["alias"] > 0:
+        prompts = rng.integers(f["lo"], f["hi"] + 1, size=f["B"])
+        seq = (prompts + 1).astype(np.int32)
+        shared = synth.alias_pages(prompts, f["alias"], 16)
+    else:
+        seq = rng.integers(f["lo"], f["hi"] + 1, size=f["B"]).astype(np.int32)
+        shared = None
+    table, num_pages, _ = synth.allocate_pages(rng, seq, 16, shared_pages=shared)
+    D = 128
+    bank_of, nb = pkv.bank_map(1, 1)
+    shape = (1, num_pages, f["hkv"], 16, D)
+    k = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), 1)
+    v = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), 2)
+    pool = pkv.Pool(torch.bfloat16, num_pages, f["hkv"], D, bank_of, nb, k=k, v=v)
+    q = synth.device_normal_(torch.empty((f["B"], f["hq"], D), dtype=torch.bfloat16,
+                                         device="cuda"), 3)
+    nk = synth.device_normal_(torch.empty((f["B"], f["hkv"], D), dtype=torch.bfloat16,
+                                          device="cuda"), 4)
+    nv = synth.device_normal_(torch.empty((f["B"], f["hkv"], D), dtype=torch.bfloat16,
+                                          device="cuda"), 5)
+    return pool, table, seq, q, nk, nv

@@ -14,8 +14,8 @@ import pytest
 
 import oracle
 from cases import oracle_decode_case, oracle_pool
-from gpu_util import (bits, check, f64, gpu_decode_case, gpu_pool, i32_dev, sample_for_oracle,
-                      tdtype, to_dev, write)
+from gpu_util import (bits, check, f64, full_size_pool, gpu_decode_case, gpu_pool, i32_dev,
+                      sample_for_oracle, tdtype, to_dev, write)
 import paged_kv_attention_kvcache_amd as pkv
 from paged_kv_attention_kvcache_amd import synth
 
@@ -361,11 +361,11 @@ def test_prefill_tile_pairs(hq, hkv):
                      gp, op)
 
 
-def test_prefill_full_size_sampled():
+def test_prefill_full_size_every_prompt():
     """The 8 x 2048 cold prefill in the launch the benchmark prices (one
     2048-token chunk of 8 prompts, 32 MHA heads, head_dim 128, written then
-    attended); the oracle checks prompts 0 and 5 on heads 0, 17 and 31, and
-    every output of the launch is finite."""
+    attended); the oracle checks every row of every prompt on heads 0, 9, 17
+    and 31, and every output of the launch is finite."""
     import torch
 
     say("prefill full-size 8 x 2048")
@@ -373,7 +373,7 @@ def test_prefill_full_size_sampled():
     chunks = synth.chunk_schedule(case, 2048)
     assert len(chunks) == 1
     out, lse = _prefill_gpu(case, chunks, gpu_pool(case.layout))[id(chunks[0])]
-    prompts, heads = [0, 5], [0, 17, 31]
+    prompts, heads = list(range(8)), [0, 9, 17, 31]
     sub = synth.PrefillCase(
         synth.Layout("bf16", 16, case.layout.num_pages, len(heads), 128), len(heads),
         case.prompt_lens[prompts], case.page_table[prompts],
@@ -451,63 +451,54 @@ def test_prefill_bitwise_shared_vs_private():
         assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
-# ------------------------------------------------------------------ full-size, sampled
+# ------------------------------------------------------------------ full-size, every row
 
 FULL = {
-    # one bank call at the full Ouro shape
-    "ouro_full": dict(B=64, lo=512, hi=2048, hq=16, hkv=8, alias=0.0, rows=[0, 31, 63]),
-    # Huginn, 78% aliased prompts
-    "huginn_full": dict(B=16, lo=200, hi=2000, hq=32, hkv=32, alias=0.78, rows=[0, 7, 15]),
+    # one bank call at the full Ouro shape: every request, every head
+    "ouro_full": dict(B=64, lo=512, hi=2048, hq=16, hkv=8, alias=0.0, kv_heads=None),
+    # Huginn, 78% aliased prompts: every request, every head
+    "huginn_full": dict(B=16, lo=200, hi=2000, hq=32, hkv=32, alias=0.78, kv_heads=None),
     # long context: 256 requests, 8k-32k context, GQA 8; the library's balanced
-    # split and the stated split-K over fixed 512-token partitions
-    "longctx_full": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255]),
-    "longctx_full_p512": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, rows=[0, 128, 255],
-                              partition=512),
+    # split and the stated split-K over fixed 512-token partitions. Every
+    # request on kv heads 0 and 5 (q heads 0-7 and 40-47): the host copy of
+    # all eight heads would be 43 GB.
+    "longctx_full": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0, kv_heads=[0, 5]),
+    "longctx_full_p512": dict(B=256, lo=8192, hi=32768, hq=64, hkv=8, alias=0.0,
+                              kv_heads=[0, 5], partition=512),
 }
 
 
 @pytest.mark.parametrize("name", sorted(FULL))
-def test_full_size_sampled(name):
+def test_full_size_every_row(name):
     """The full workload in the launch configuration the benchmark times; the
-    oracle checks a sample of requests one by one."""
+    oracle checks every request (on every kv head, or on two for the long
+    context), element by element."""
     import torch
 
     f = FULL[name]
     say(f"full-size {name}")
-    rng = np.random.default_rng(11)
-    if f["alias"] > 0:
-        prompts = rng.integers(f["lo"], f["hi"] + 1, size=f["B"])
-        seq = (prompts + 1).astype(np.int32)
-        shared = synth.alias_pages(prompts, f["alias"], 16)
-    else:
-        seq = rng.integers(f["lo"], f["hi"] + 1, size=f["B"]).astype(np.int32)
-        shared = None
-    table, num_pages, _ = synth.allocate_pages(rng, seq, 16, shared_pages=shared)
-    D = 128
-    bank_of, nb = pkv.bank_map(1, 1)
-    shape = (1, num_pages, f["hkv"], 16, D)
-    k = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), 1)
-    v = synth.device_normal_(torch.empty(shape, dtype=torch.bfloat16, device="cuda"), 2)
-    pool = pkv.Pool(torch.bfloat16, num_pages, f["hkv"], D, bank_of, nb, k=k, v=v)
-    q = synth.device_normal_(torch.empty((f["B"], f["hq"], D), dtype=torch.bfloat16,
-                                         device="cuda"), 3)
-    nk = synth.device_normal_(torch.empty((f["B"], f["hkv"], D), dtype=torch.bfloat16,
-                                          device="cuda"), 4)
-    nv = synth.device_normal_(torch.empty((f["B"], f["hkv"], D), dtype=torch.bfloat16,
-                                          device="cuda"), 5)
-    slots = synth.slots_of_last(table, seq, 16)
-    rows = f["rows"]
-    # the oracle's copy of the sampled requests, taken before any kernel runs
-    opool, otable = sample_for_oracle(k[0], v[0], table, seq, rows, "bf16")
-    oracle.kv_write(opool, 0, 0, bits(nk)[rows], bits(nv)[rows],
-                    synth.slots_of_last(otable, seq[rows], 16))
-    ro, rl = oracle.decode(opool, 0, 0, bits(q)[rows], otable, seq[rows])
+    pool, table, seq, q, nk, nv = full_size_pool(f)
+    k, v = pool.k, pool.v
+    G = f["hq"] // f["hkv"]
+    heads = list(range(f["hkv"])) if f["kv_heads"] is None else f["kv_heads"]
+    qheads = [h * G + g for h in heads for g in range(G)]
+    rows = np.arange(f["B"])
+    hidx = torch.tensor(heads, device="cuda")
+    # the oracle's copy of the sampled kv heads, taken before any kernel runs
+    opool, otable = sample_for_oracle(k[0].index_select(1, hidx), v[0].index_select(1, hidx),
+                                      table, seq, rows, "bf16")
+    oracle.kv_write(opool, 0, 0, bits(nk)[:, heads], bits(nv)[:, heads],
+                    synth.slots_of_last(otable, seq, 16))
+    ro, rl = oracle.decode(opool, 0, 0, np.ascontiguousarray(bits(q)[:, qheads]), otable, seq)
+    del opool
     # the GPU path: write the new token, then decode, as the benchmark does
+    slots = synth.slots_of_last(table, seq, 16)
     pkv.kv_write(pool, 0, 0, nk, nv, i32_dev(slots))
     out, lse = pkv.decode(pool, 0, 0, q, i32_dev(table), i32_dev(seq), int(seq.max()),
                           partition=f.get("partition", 0))
     torch.cuda.synchronize()
-    check(name, "bf16", f64(out)[rows], ro, rl, lse[rows])
-    # every row of the full batch is finite (no stray read of poison or of
-    # another request's partials)
+    qh = torch.tensor(qheads, device="cuda")
+    check(name, "bf16", out.index_select(1, qh), ro, rl, lse.index_select(1, qh))
+    # the rows of heads outside the sample are finite (no stray read of
+    # poison or of another request's partials)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
