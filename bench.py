@@ -7,16 +7,27 @@ decode attention reads the whole context through the page table. By default
 both happen in one call (paged_decode_append_attn); --separate-write issues
 paged_kv_write then paged_decode_attn instead (same results, bit for bit).
 
-Default workload (Ouro-style fixed depth): 24 layers x 4 loop planes = 96
-banks, batch 64, seq_lens uniform in [512, 2048], page size 16, 16 query / 8
-KV heads, head_dim 128, bf16, pages randomly permuted. Other workloads:
---workload huginn (132 packed banks, MHA 32 heads, 78% aliased prompt pages),
---workload longctx (batch 256, 8k-32k context, GQA 8, one bank), --workload
-prefill (chunked prefill, 8 x 512-token prompts, 32 heads).
+The headline (the top-level value, ms_per_step, roofline and cpu_baseline) is
+the Ouro-style fixed-depth step: 24 layers x 4 loop planes = 96 banks, batch
+64, seq_lens uniform in [512, 2048], page size 16, 16 query / 8 KV heads,
+head_dim 128, bf16, pages randomly permuted. The same run measures every
+other workload under "configs", each with the roofline of its dominant kernel
+and the fp64 oracle timed on a stated sample:
+  tiny_decode                     fp32, 4 requests of 17-64 tokens (launch-bound)
+  huginn_recurrent_depth_decode   132 packed banks, MHA 32 heads, 78% aliased
+                                  prompt pages (logical and unique bytes)
+  cached_prefix_prefill           8 x 512-token prompts: cold chunk 2048,
+                                  cold chunk 128, 16-token suffix over 496
+  long_context_decode             batch 256, 8k-32k contexts, GQA 8: the
+                                  library's balanced split and the stated
+                                  fixed 512-token partitions
+  prefill_8x2048                  8 cold 2048-token prompts in one chunk
+--workload huginn|longctx times one of the decode workloads alone (its own
+headline line), --prefill-only the prefill cases alone.
 
-Prints one JSON line. `value` is logical KV bytes read by decode attention
-per second over the whole step (write + attention for every bank), with all
-inputs resident in HBM before the timed region starts.
+`value` is logical KV bytes read by decode attention per second over the
+whole step (write + attention for every bank), with all inputs resident in
+HBM before the timed region starts.
 """
 from __future__ import annotations
 
@@ -41,18 +52,42 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_from_profiles(workload: str, launches_per_unit: float = 1.0):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, or None when it was taken on different kernel sources."""
+def profile_for(workload: str):
+    """The committed rocprofv3 figures of one workload (profiles/kernels.json):
+    {"us_per_call": summed kernel averages of one call, "hbm_bytes_per_call":
+    counter-measured HBM bytes, "kernels": [...]}, or None when they were
+    taken on other sources than the ones built here."""
     from paged_kv_attention_kvcache_amd.rocprof_summary import kernel_source_hash
 
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", "kernels.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("workloads", {}).get(workload)
+
+
+def roofline(workload: str, kernel: str, achieved: float, peak: float, unit: str,
+             bound: str, per_call: float, call_s: float, **extra) -> dict:
+    """The roofline object of a workload's dominant kernel: `achieved` from
+    the live HIP-event time of one call (per_call algorithmic bytes or flops /
+    call_s); beside it the same call priced with the committed rocprofv3
+    kernel averages, and the counter-measured HBM traffic, when those were
+    taken on these sources."""
+    prof = profile_for(workload)
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4),
+         "traffic": prof.get("hbm_bytes_per_call") if prof else None,
+         "kernel": kernel, "hip_event_us_per_call": round(call_s * 1e6, 3)}
+    if prof:
+        us = prof["us_per_call"]
+        scale = 1e9 if unit == "GB/s" else 1e12
+        r["profiled_us_per_call"] = us
+        r["achieved_profiled"] = round(per_call / (us * 1e-6) / scale, 2)
+        r["frac_profiled"] = round(per_call / (us * 1e-6) / scale / peak, 4)
+    r.update(extra)
+    return r
 
 
 # --------------------------------------------------------------------------- workloads
@@ -61,7 +96,8 @@ class DecodeWorkload:
     """A multi-plane pool and one decode step's inputs, all on the device."""
 
     def __init__(self, name, batch, seq_range, hq, hkv, D, planes, layers, rec_first,
-                 rec_count, order, alias=0.0, partition=0, seed=0, snapshot_banks=0):
+                 rec_count, order, alias=0.0, partition=0, seed=0, snapshot_banks=0,
+                 snapshot_rows=0):
         import torch
 
         import paged_kv_attention_kvcache_amd as pkv
@@ -116,12 +152,30 @@ class DecodeWorkload:
             [self.table[r, :-(-int(n) // 16)] for r, n in enumerate(self.seq)])))
         self.unique_bytes_per_call = uniq_pages * 2 * hkv * 16 * D * 2
         torch.cuda.synchronize()
-        # Host copies for the CPU baseline, taken before any library kernel runs.
+        # Host copies for the CPU baseline, taken before any library kernel runs:
+        # whole banks of the first calls of the step, or the pages of the first
+        # snapshot_rows requests of the first call's bank (renumbered).
+        hb = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         self.snap = []
         for i in range(min(snapshot_banks, len(order))):
             b = int(self.bank_of[order[i]])
-            hb = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-            self.snap.append((hb(k[b])[None], hb(v[b])[None], hb(self.q[i])))
+            self.snap.append((hb(k[b])[None], hb(v[b])[None], hb(self.q[i]), self.table,
+                              self.seq, self.kv_bytes_per_call))
+        if snapshot_rows:
+            rows = np.arange(min(snapshot_rows, batch))
+            b = int(self.bank_of[order[0]])
+            need = [self.table[r, :-(-int(self.seq[r]) // 16)] for r in rows]
+            uniq = np.unique(np.concatenate(need))
+            remap = np.zeros(self.num_pages, np.int32)
+            remap[uniq] = np.arange(len(uniq), dtype=np.int32)
+            idx = torch.from_numpy(uniq.astype(np.int64)).cuda()
+            table = np.zeros((len(rows), self.table.shape[1]), np.int32)
+            for i, r in enumerate(rows):
+                table[i, :len(need[i])] = remap[need[i]]
+            seq = self.seq[rows]
+            self.snap.append((hb(k[b].index_select(0, idx))[None],
+                              hb(v[b].index_select(0, idx))[None], hb(self.q[0][rows]), table,
+                              seq, int(seq.astype(np.int64).sum()) * 2 * hkv * D * 2))
 
     def kernel_for(self, split, partition):
         """The decode kernels a call of this workload launches."""
@@ -210,8 +264,8 @@ class DecodeWorkload:
                              k_new=self.nk, v_new=self.nv, partition=self.partition)
 
 
-def make_workload(name, partition, snapshot_banks=0):
-    kw = dict(partition=partition, snapshot_banks=snapshot_banks)
+def make_workload(name, partition, snapshot_banks=0, snapshot_rows=0):
+    kw = dict(partition=partition, snapshot_banks=snapshot_banks, snapshot_rows=snapshot_rows)
     if name == "ouro":
         order = [(t, l) for t in range(4) for l in range(24)]
         return DecodeWorkload("ouro", 64, (512, 2048), 16, 8, 128, 4, 24, 0, 24, order, **kw)
@@ -286,7 +340,7 @@ class PrefillWorkload:
                                     for r in range(self.prompts)])
             rows = np.concatenate([r * self.n + np.arange(lo, hi) for r in range(self.prompts)])
             pairs = self.prompts * sum(p + 1 for p in range(lo, hi))
-            out.append(dict(slots=torch.from_numpy(slots).cuda(),
+            out.append(dict(start=start, slots=torch.from_numpy(slots).cuda(),
                             rows=torch.from_numpy(rows.astype(np.int64)).cuda(),
                             cu=torch.from_numpy(np.arange(0, self.prompts + 1, dtype=np.int32)
                                                 * q_len).cuda(),
@@ -316,48 +370,111 @@ class PrefillWorkload:
                         c["hi"], out=c["o"], with_lse=False)
 
 
-def run_prefill(reps=3, supplementary=True):
-    """TFLOP/s of causal prefill: 4 * head_dim * heads * (visible query-key
-    pairs) algorithmic flops per call, written then attended."""
+PREFILL_CASES = [
+    # (name, prompts, tokens per prompt, chunk, cached prefix tokens)
+    ("cold_chunk2048", 8, 512, 2048, 0),
+    ("cold_chunk128", 8, 512, 128, 0),
+    ("suffix16_over_496", 8, 512, 4096, 496),
+]
+SUPPLEMENTARY = ("cold_2048x8_chunk2048", 8, 2048, 2048, 0)
+
+
+def time_prefill_case(wl, chunks, reps):
+    """Per call of the case (all its chunks): write-then-attend, the one-call
+    extend, and the attention alone, each over reps rounds of the bank
+    rotation, between HIP events on the stream the library launches on."""
     import torch
 
+    stream = torch.cuda.current_stream()
+    for b in range(2):
+        wl.run(chunks, b)
+    torch.cuda.synchronize()
+    out = {}
+    for write in (True, "extend", False):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nbk = wl.nb
+        a.record(stream)
+        for i in range(reps * nbk):
+            wl.run(chunks, i % nbk, write=write)
+        e.record(stream)
+        torch.cuda.synchronize()
+        key = {True: "write_then_attend", "extend": "extend_one_call",
+               False: "attend_only"}[write]
+        out[key] = a.elapsed_time(e) / 1e3 / (reps * nbk)
+    return out
+
+
+def cpu_prefill(wl, chunks, budget_s):
+    """The fp64 oracle on the first chunk's call of a prefill case (all its
+    prompts and heads), on host copies of the chunk's K/V/Q written into a
+    pool of its own: TFLOP/s of the same algorithmic flops."""
+    import oracle
+
+    c = chunks[0]
+    hb = lambda t: t.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    bank_of = np.zeros((1, 1), np.int32)
+    op = oracle.Pool("bf16", 16, wl.num_pages, wl.heads, wl.D, bank_of, 1)
+    if c["start"]:  # the cached prefix, as the generator left it in the pool
+        op.k[0] = hb(wl.pool.k[0])
+        op.v[0] = hb(wl.pool.v[0])
+    oracle.kv_write(op, 0, 0, hb(c["k"]), hb(c["v"]), c["slots"].cpu().numpy())
+    q, cu = hb(c["q"]), c["cu"].cpu().numpy()
+    seq = c["seq"].cpu().numpy()
+    flops = 4 * wl.D * wl.heads * c["pairs"]
+    done, spent, calls = 0, 0.0, 0
+    while spent < budget_s and (calls == 0 or spent + spent / calls <= budget_s):
+        t0 = time.perf_counter()
+        oracle.prefill(op, 0, 0, q, cu, wl.table, seq)
+        spent += time.perf_counter() - t0
+        done += flops
+        calls += 1
+    return {"value": round(done / spent / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", "1")), "kind": "oracle",
+            "sample": f"{calls} x the first call of the case ({wl.prompts} prompts x "
+                      f"{c['q_len']} query rows, {wl.heads} heads, fp64 oracle), {spent:.2f} s"}
+
+
+def run_prefill(reps=3, supplementary=True, cpu_budget=0.0):
+    """TFLOP/s of causal prefill: 4 * head_dim * heads * (visible query-key
+    pairs) algorithmic flops per call, written then attended. The cached-prefix
+    cases are calls over 8 x 512-token prompts, rotating over 132 banks; the
+    supplementary case 8 cold 2048-token prompts, rotating over 24 banks."""
     res = {}
-    cases = [("cold_chunk2048", 8, 512, 2048, 0), ("cold_chunk128", 8, 512, 128, 0),
-             ("suffix16_over_496", 8, 512, 4096, 496)]
-    if supplementary:
-        cases.append(("cold_2048x8_chunk2048", 8, 2048, 2048, 0))
+    cases = list(PREFILL_CASES) + ([SUPPLEMENTARY] if supplementary else [])
     wls = {}
     for name, prompts, n, chunk, start in cases:
         if (prompts, n) not in wls:
             wls[(prompts, n)] = PrefillWorkload(prompts, n, banks=132 if n <= 512 else 24)
         wl = wls[(prompts, n)]
         chunks = wl.schedule(chunk, start)
-        if start:  # the cached prefix is already in every bank (from the generator)
-            pass
         flops = 4 * wl.D * wl.heads * sum(c["pairs"] for c in chunks)
         hbm = sum(c["hi"] * wl.prompts * 2 * wl.heads * wl.D * 2 + 2 * c["q"].numel() * 2
                   for c in chunks)
-        for b in range(2):
-            wl.run(chunks, b)
-        torch.cuda.synchronize()
+        t = time_prefill_case(wl, chunks, reps)
         out = {}
-        for write in (True, "extend", False):
-            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            nbk = wl.nb
-            a.record()
-            for i in range(reps * nbk):
-                wl.run(chunks, i % nbk, write=write)
-            e.record()
-            torch.cuda.synchronize()
-            sec = a.elapsed_time(e) / 1e3 / (reps * nbk)
-            key = {True: "write_then_attend", "extend": "extend_one_call",
-                   False: "attend_only"}[write]
+        for key, sec in t.items():
             out[key] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 2),
                         "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                         "hbm_GBps": round(hbm / sec / 1e9, 1),
                         "hbm_frac": round(hbm / sec / 1e9 / HBM_PEAK_GBS, 4)}
+        out["calls_per_case"] = len(chunks)
         out["flops"] = flops
         out["algorithmic_bytes"] = hbm
+        sec = t["attend_only"] / len(chunks)
+        if name == "cold_chunk2048":
+            out["roofline"] = roofline(
+                "prefill_cold2048", "prefill_mfma<4, 2, 2048> (8 x 512 rows, 4 tiles each)",
+                flops / sec / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma", flops, sec,
+                hbm_frac=round(hbm / sec / 1e9 / HBM_PEAK_GBS, 4),
+                note="at the ridge: 128 flop per algorithmic byte; the HBM floor of the "
+                     "call is 16.8 us")
+        if name == SUPPLEMENTARY[0]:
+            out["roofline"] = roofline(
+                "prefill_8x2048", "prefill_mfma<4, 2, 2048> (8 x 2048 rows, 16 tiles each)",
+                flops / sec / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma", flops, sec)
+        if cpu_budget > 0 and name in ("cold_chunk2048", "suffix16_over_496"):
+            log(f"cpu baseline (oracle): prefill {name} ...")
+            out["cpu_baseline"] = cpu_prefill(wl, chunks, cpu_budget)
         res[name] = out
         log(f"prefill {name}: {out}")
     return res
@@ -416,40 +533,33 @@ def run_lotus(prompts=8, prompt_len=512, block=64, loop_iters=4, heads=32, D=128
     return res
 
 
-def run_latest_bank(steps=10, warmup=2):
-    """A Huginn-shaped decode step (132 bank calls) where context tokens
-    halted early at depths uniform in [20, 31] and recurrent-layer calls read
-    each token from its latest bank, next to the same step without early
-    exit. Logical KV bytes are the same in both."""
+def run_latest_bank(wl, steps=10, warmup=2):
+    """The Huginn-shaped step where context tokens halted early at depths
+    uniform in [20, 31] and recurrent-layer calls read each token from its
+    latest bank (paged_decode_latest_attn), timed on the same workload after
+    its ordinary step. Logical KV bytes are the same in both."""
     import torch
 
-    wl = make_workload("huginn", 0)
-    out = {}
-    for mode in ("all_planes", "latest_bank"):
-        if mode == "latest_bank":
-            wl.use_exit_depths(20, 31)
-        for _ in range(warmup):
-            wl.step()
-        torch.cuda.synchronize()
-        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(steps):
-            wl.step()
-        e.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(e) / steps
-        out[mode] = {"ms_per_step": round(ms, 4),
-                     "kv_GBps": round(wl.kv_bytes_per_call * len(wl.order) / (ms / 1e3) / 1e9,
-                                      2)}
-    out["exit_depths"] = "uniform[20,31] per context token"
-    out["how"] = "paged_decode_latest_attn for plane >= 1 (store_kv of the newest token fused)"
-    log(f"latest bank: {out}")
-    del wl
-    torch.cuda.empty_cache()
-    return out
+    stream = torch.cuda.current_stream()
+    wl.use_exit_depths(20, 31)
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        wl.step()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / steps
+    wl.exit_depth = None
+    return {"ms_per_step": round(ms, 4),
+            "kv_GBps_logical": round(wl.kv_bytes_per_call * len(wl.order) / (ms / 1e3) / 1e9, 2),
+            "exit_depths": "uniform[20,31] per context token",
+            "how": "paged_decode_latest_attn for plane >= 1 (store_kv of the newest token fused)"}
 
 
-def run_tiny(reps=500):
+def run_tiny(reps=500, cpu_budget=0.0):
     """The tiny decode shape (fp32, 4 requests of 17-64 tokens, 4 query / 2 kv
     heads, head_dim 64, a 64-page pool): the fused store_kv + attention call,
     timed per call. At about 166 KB of KV it measures launch latency, not
@@ -488,8 +598,29 @@ def run_tiny(reps=500):
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
     kv = int(case.seq_lens.sum()) * 2 * 2 * 64 * 4
-    return {"us_per_call": round(us, 3), "kv_bytes": kv, "kv_GBps": round(kv / us / 1e3, 2),
-            "how": "paged_decode_append_attn back to back on one stream (launch-bound)"}
+    res = {"config": dict(workload="tiny_decode", batch=4, seq_lens="uniform[17,64]",
+                          q_heads=4, kv_heads=2, head_dim=64, dtype="fp32", num_pages=64),
+           "us_per_call": round(us, 3), "kv_bytes": kv, "kv_GBps": round(kv / us / 1e3, 2),
+           "how": "paged_decode_append_attn back to back on one stream (launch-bound; "
+                  "not held to the HBM bar)"}
+    if cpu_budget > 0:
+        import oracle
+
+        op = oracle.Pool("f32", 16, 64, 2, 64, bank_of, nb)
+        oracle.kv_write(op, 0, 0, bd.fill_k, bd.fill_v, bd.fill_slots)
+        oracle.kv_write(op, 0, 0, bd.new_k, bd.new_v, bd.new_slots)
+        spent, calls = 0.0, 0
+        while spent < cpu_budget:
+            t0 = time.perf_counter()
+            oracle.decode(op, 0, 0, bd.q, case.page_table, case.seq_lens)
+            spent += time.perf_counter() - t0
+            calls += 1
+        res["cpu_baseline"] = {
+            "value": round(spent / calls * 1e6, 3), "unit": "us per call",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", "1")), "kind": "oracle",
+            "sample": f"{calls} calls of the whole tiny decode (4 requests, 4 heads; the "
+                      f"oracle's attention alone, its store_kv done once), {spent:.2f} s"}
+    return res
 
 
 def run_page_mgr(reps=200):
@@ -527,147 +658,208 @@ def run_page_mgr(reps=200):
 
 # --------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(wl: DecodeWorkload, budget_s: float = 15.0):
-    """The fp64 oracle, as it stands, on whole bank calls of the same step
-    (host copies taken before any library kernel ran) until about budget_s of
-    CPU time; scaled to KV GB/s like the GPU value."""
-    import oracle
-
+def cpu_threads() -> int:
+    """Threads the oracle runs with: every core this process may use."""
     threads = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    cores = int(os.environ["OMP_NUM_THREADS"])
+    return int(os.environ["OMP_NUM_THREADS"])
+
+
+def cpu_baseline(wl: DecodeWorkload, budget_s: float = 8.0):
+    """The fp64 oracle, as it stands, on the workload's host snapshots (whole
+    banks of the step, or a subset of the requests of one bank, copied before
+    any library kernel ran) until about budget_s of CPU time; scaled to
+    logical KV GB/s like the GPU value."""
+    import oracle
+
+    cores = cpu_threads()
     done_bytes, spent, calls = 0, 0.0, 0
     bank_of = np.zeros((1, 1), np.int32)
-    pools = [(oracle.Pool("bf16", 16, wl.num_pages, wl.hkv, wl.D, bank_of, 1, k, v), q)
-             for k, v, q in wl.snap]
+    pools = [(oracle.Pool("bf16", 16, k.shape[1], wl.hkv, wl.D, bank_of, 1, k, v), q, t, n, b)
+             for k, v, q, t, n, b in wl.snap]
     while pools and spent < budget_s:
-        for op, q in pools:
+        for op, q, table, seq, nbytes in pools:
             t0 = time.perf_counter()
-            oracle.decode(op, 0, 0, q, wl.table, wl.seq)
+            oracle.decode(op, 0, 0, q, table, seq)
             spent += time.perf_counter() - t0
-            done_bytes += wl.kv_bytes_per_call
+            done_bytes += nbytes
             calls += 1
             if spent >= budget_s:
                 break
+    rows = len(wl.snap[0][4]) if wl.snap else 0
+    what = (f"{len(wl.snap)} distinct banks of the {len(wl.order)} in one {wl.name} step, "
+            f"{wl.batch} requests, all heads" if rows == wl.batch else
+            f"the first {rows} of the {wl.batch} requests of one call, all heads")
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{calls} bank decode calls ({len(wl.snap)} distinct banks of the "
-                      f"{len(wl.order)} in one {wl.name} step, {wl.batch} requests, all heads), "
-                      f"fp64 oracle, {spent:.1f} s"}
+            "sample": f"{calls} oracle decode calls over {what}; logical KV bytes of those "
+                      f"calls / {spent:.1f} s (fp64)"}
 
 
-# --------------------------------------------------------------------------- main
+# --------------------------------------------------------------------------- decode configs
 
-def run_decode(args):
+def time_decode(wl, steps, warmup, graph=True):
+    """Times wl's step: K whole steps between two HIP events on the stream
+    the library launches on; per-step spread; the decode calls alone back to
+    back (the dominant kernel's time per call); and the step replayed as one
+    submission."""
     import torch
 
-    wl = make_workload(args.workload, args.partition,
-                       0 if args.no_cpu_baseline else args.cpu_banks)
-    wl.separate_write = args.separate_write
     nb = len(wl.order)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
-
-    # Timed region: K whole steps, events on the stream the library launches on.
     stream = torch.cuda.current_stream()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         wl.step()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-
-    # Per-step spread: K more steps, each between its own pair of events (after
-    # the timed region, so that region is K steps and nothing else).
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ms_per_step = t0.elapsed_time(t1) / steps
+    # Per-step spread: K more steps, each between its own pair of events
+    # (after the timed region, so that region is K steps and nothing else).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
-    for k in range(args.steps):
+    for k in range(steps):
         wl.step()
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
-    per_step = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])
+    per_step = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(steps)])
     spread = {f"p{q}": round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)}
-
-    # The decode calls alone, back to back over K rounds of every bank, between
-    # two events on the stream the library launches on: the average duration
-    # of the dominant kernel (its combine kernel included when the split
-    # needs one; the fused store_kv included when the step fuses it).
-    torch.cuda.synchronize()
+    # The decode calls alone, back to back over K rounds of every bank.
     d0 = torch.cuda.Event(enable_timing=True)
     d1 = torch.cuda.Event(enable_timing=True)
     d0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         for i in range(nb):
             wl.call(i, decode_only=True)
     d1.record(stream)
     torch.cuda.synchronize()
-    avg_call_s = d0.elapsed_time(d1) / 1e3 / (args.steps * nb)
-    step_bytes = wl.kv_bytes_per_call * nb
+    call_s = d0.elapsed_time(d1) / 1e3 / (steps * nb)
+    res = {"ms_per_step": ms_per_step, "spread": spread, "call_s": call_s, "wall_s": wall}
+    if graph:
+        g = wl.step_graph()
+        for _ in range(max(warmup, 1)):
+            g.launch(stream)
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(steps):
+            g.launch(stream)
+        g1.record(stream)
+        torch.cuda.synchronize()
+        res["graph_ms"] = g0.elapsed_time(g1) / steps
+        g.close()
+    return res
 
-    # The same step as one submission (paged_decode_step captured once, then
-    # replayed): K replays between two events.
-    graph = wl.step_graph()
-    for _ in range(max(args.warmup, 1)):
-        graph.launch(stream)
-    torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record(stream)
-    for _ in range(args.steps):
-        graph.launch(stream)
-    g1.record(stream)
-    torch.cuda.synchronize()
-    graph_ms = g0.elapsed_time(g1) / args.steps
-    graph.close()
-    value = step_bytes / (ms_per_step / 1e3) / 1e9
-    achieved = wl.kv_bytes_per_call / avg_call_s / 1e9
-    res = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) K/V/Q, random page permutation)",
-        "config": dict(CONFIG_TEXT[wl.name], partition=wl.partition),
-        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
-        "ms_per_step_spread": spread,
-        "tokens_planes_per_s": round(wl.batch * nb / (ms_per_step / 1e3), 1),
-        "single_submission": {"ms_per_step": round(graph_ms, 4),
-                              "kv_GBps": round(step_bytes / (graph_ms / 1e3) / 1e9, 2),
-                              "tokens_planes_per_s": round(wl.batch * nb / (graph_ms / 1e3), 1),
-                              "how": "paged_decode_step_capture + graph launch per step"},
-        "step": "paged_kv_write + paged_decode_attn" if wl.separate_write
-                else "paged_decode_append_attn (store_kv of the newest token fused)",
-        "decode_call_us": round(avg_call_s * 1e6, 2),
-        "split": wl.split,
-        "kv_bytes_per_call": wl.kv_bytes_per_call,
-        "unique_kv_bytes_per_call": wl.unique_bytes_per_call,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_from_profiles(wl.name),
-                     "kernel": wl.kernel_name},
-        "wall_s_timed": round(wall, 3),
-    }
-    if wl.name == "longctx" and wl.split != "fixed":
-        # the split this workload states: fixed 512-token partitions
-        res["fixed_partition_512"] = wl.time_fixed_partitions(512, args.steps, stream)
-        log(f"fixed partitions: {res['fixed_partition_512']}")
+
+def decode_summary(wl, t):
+    """The step's figures: logical KV GB/s over the whole step, its share of
+    HBM peak, tokens x planes per second, and the single-submission replay."""
+    nb = len(wl.order)
+    step_bytes = wl.kv_bytes_per_call * nb
+    gbs = step_bytes / (t["ms_per_step"] / 1e3) / 1e9
+    out = {"ms_per_step": round(t["ms_per_step"], 4),
+           "ms_per_step_spread": t["spread"],
+           "kv_GBps": round(gbs, 2),
+           "hbm_frac_step": round(gbs / HBM_PEAK_GBS, 4),
+           "tokens_planes_per_s": round(wl.batch * nb / (t["ms_per_step"] / 1e3), 1),
+           "decode_call_us": round(t["call_s"] * 1e6, 2),
+           "split": wl.split,
+           "kv_bytes_per_call": wl.kv_bytes_per_call,
+           "unique_kv_bytes_per_call": wl.unique_bytes_per_call}
+    if "graph_ms" in t:
+        g = t["graph_ms"]
+        out["single_submission"] = {
+            "ms_per_step": round(g, 4), "kv_GBps": round(step_bytes / (g / 1e3) / 1e9, 2),
+            "tokens_planes_per_s": round(wl.batch * nb / (g / 1e3), 1),
+            "how": "paged_decode_step_capture + graph launch per step"}
+    return out
+
+
+def run_ouro(args):
+    """The headline: the Ouro-shaped 96-bank step."""
+    wl = make_workload("ouro", args.partition, 0 if args.no_cpu_baseline else args.cpu_banks)
+    wl.separate_write = args.separate_write
+    t = time_decode(wl, args.steps, args.warmup)
+    res = decode_summary(wl, t)
+    achieved = wl.kv_bytes_per_call / t["call_s"] / 1e9
+    res["roofline"] = roofline("ouro", wl.kernel_name, achieved, HBM_PEAK_GBS, "GB/s", "hbm",
+                               wl.kv_bytes_per_call, t["call_s"],
+                               bytes="logical K+V of every request's context per call")
+    res["step"] = ("paged_kv_write + paged_decode_attn" if wl.separate_write
+                   else "paged_decode_append_attn (store_kv of the newest token fused)")
+    res["wall_s_timed"] = round(t["wall_s"], 3)
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
+        log("cpu baseline (oracle): ouro ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
-    return res, wl
+    return res
+
+
+def run_huginn(args, steps=None):
+    """The Huginn-shaped 132-bank step, 78% of prompt pages aliased: logical
+    and unique bytes, and the early-exit variant of the same step."""
+    import torch
+
+    steps = steps or args.steps
+    wl = make_workload("huginn", 0, 0 if args.no_cpu_baseline else args.cpu_banks)
+    t = time_decode(wl, steps, args.warmup)
+    res = decode_summary(wl, t)
+    nb = len(wl.order)
+    uniq = wl.unique_bytes_per_call * nb / (t["ms_per_step"] / 1e3) / 1e9
+    res["kv_GBps_logical"] = res.pop("kv_GBps")
+    res["hbm_frac_logical"] = res.pop("hbm_frac_step")
+    res["kv_GBps_unique"] = round(uniq, 2)
+    res["hbm_frac_unique"] = round(uniq / HBM_PEAK_GBS, 4)
+    achieved = wl.unique_bytes_per_call / t["call_s"] / 1e9
+    res["roofline"] = roofline(
+        "huginn", wl.kernel_name, achieved, HBM_PEAK_GBS, "GB/s", "hbm",
+        wl.unique_bytes_per_call, t["call_s"],
+        bytes="unique K+V pages per call (each aliased prefix page once)",
+        achieved_logical=round(wl.kv_bytes_per_call / t["call_s"] / 1e9, 2))
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle): huginn ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget / 2)
+    res["config"] = CONFIG_TEXT["huginn"]
+    res["latest_bank"] = run_latest_bank(wl, steps=min(steps, 10))
+    log(f"huginn: {res}")
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_longctx(args, steps=None):
+    """One long-context call (batch 256, 8k-32k tokens, GQA 8): the library's
+    balanced split, then the stated split-K over fixed 512-token partitions."""
+    import torch
+
+    steps = steps or args.steps
+    wl = make_workload("longctx", 0, 0, 0 if args.no_cpu_baseline else 32)
+    t = time_decode(wl, steps, args.warmup, graph=False)
+    res = {"balanced": decode_summary(wl, t)}
+    achieved = wl.kv_bytes_per_call / t["call_s"] / 1e9
+    res["balanced"]["roofline"] = roofline(
+        "longctx", wl.kernel_name, achieved, HBM_PEAK_GBS, "GB/s", "hbm", wl.kv_bytes_per_call,
+        t["call_s"], bytes="logical K+V of every request's context per call")
+    fx = wl.time_fixed_partitions(512, steps, torch.cuda.current_stream())
+    fx["roofline"] = roofline(
+        "longctx_p512", fx["kernel"], fx["kv_GBps"], HBM_PEAK_GBS, "GB/s", "hbm",
+        wl.kv_bytes_per_call, fx["us_per_call"] / 1e6,
+        bytes="logical K+V of every request's context per call")
+    res["fixed_partition_512"] = fx
+    res["config"] = CONFIG_TEXT["longctx"]
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle): longctx ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget / 2)
+    log(f"longctx: {res}")
+    del wl
+    torch.cuda.empty_cache()
+    return res
 
 
 def run_probe(kind: str):
@@ -700,10 +892,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="ouro", choices=["ouro", "huginn", "longctx"])
+    ap.add_argument("--workload", default="all", choices=["all", "ouro", "huginn", "longctx"],
+                    help="all (default): the Ouro headline plus every other workload under "
+                         "configs; otherwise one decode workload alone")
     ap.add_argument("--partition", type=int, default=0)
     ap.add_argument("--no-prefill", action="store_true",
-                    help="skip the chunked-prefill measurement")
+                    help="skip the prefill cases and the LOTUS loop")
     ap.add_argument("--no-supplementary", action="store_true",
                     help="skip the 8 x 2048-token prefill shape")
     ap.add_argument("--prefill-only", action="store_true",
@@ -711,7 +905,9 @@ def main():
     ap.add_argument("--separate-write", action="store_true",
                     help="paged_kv_write + paged_decode_attn per bank instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle time for the headline's CPU baseline (half that "
+                         "for the Huginn and long-context ones)")
     ap.add_argument("--probe", choices=["copy", "read"], default=None,
                     help="time a plain copy/read of 1 GiB instead (counter calibration)")
     ap.add_argument("--cpu-banks", type=int, default=4,
@@ -731,23 +927,60 @@ def main():
     if args.probe:
         print(json.dumps(run_probe(args.probe)), flush=True)
         return
+    if not args.no_cpu_baseline:
+        cpu_threads()
+    cpu = 0.0 if args.no_cpu_baseline else 1.0
     log(f"device: {torch.cuda.get_device_name(0)}; workload {args.workload}")
     if args.prefill_only:
-        print(json.dumps({"prefill": run_prefill(supplementary=not args.no_supplementary),
+        print(json.dumps({"prefill": run_prefill(supplementary=not args.no_supplementary,
+                                                 cpu_budget=cpu),
                           "lotus": run_lotus()}), flush=True)
         return
-    res, wl = run_decode(args)
-    if not args.no_prefill:
-        del wl
+    if args.workload in ("huginn", "longctx"):
+        res = run_huginn(args) if args.workload == "huginn" else run_longctx(args)
+        print(json.dumps({"metric": METRIC, "workload": CONFIG_TEXT[args.workload]["workload"],
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "config": CONFIG_TEXT[args.workload], **res}), flush=True)
+        return
+    ouro = run_ouro(args)
+    res = {
+        "metric": METRIC,
+        "value": ouro["kv_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ouro["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/Q, random page permutation)",
+        "config": dict(CONFIG_TEXT["ouro"], partition=args.partition),
+        "roofline": ouro["roofline"],
+    }
+    if "cpu_baseline" in ouro:
+        res["cpu_baseline"] = ouro["cpu_baseline"]
+    configs = {"ouro_fixed_depth_decode": ouro}
+    if args.workload == "all":
         torch.cuda.empty_cache()
-        res["prefill"] = run_prefill(supplementary=not args.no_supplementary)
-        res["lotus"] = run_lotus()
-        res["latest_bank"] = run_latest_bank()
-        res["tiny_decode"] = run_tiny()
-        torch.cuda.empty_cache()
-        res["hbm_probe"] = {k: run_probe(k)["GBps"] for k in ("copy", "read")}
-        res["hbm_probe"]["how"] = ("torch copy_ (read + write) and max (read) of 1 GiB: "
-                                   "the bandwidth a library kernel reaches")
+        configs["tiny_decode"] = run_tiny(cpu_budget=cpu)
+        configs["huginn_recurrent_depth_decode"] = run_huginn(args)
+        configs["long_context_decode"] = run_longctx(args)
+        if not args.no_prefill:
+            pf = run_prefill(supplementary=not args.no_supplementary, cpu_budget=cpu)
+            configs["cached_prefix_prefill"] = {k: pf[k] for k, *_ in PREFILL_CASES}
+            configs["cached_prefix_prefill"]["config"] = dict(
+                workload="cached_prefix_prefill", prompts=8, tokens=512, cached_tokens=496,
+                heads=32, head_dim=128, page_size=16, banks_rotated=132)
+            if SUPPLEMENTARY[0] in pf:
+                configs["prefill_8x2048"] = pf[SUPPLEMENTARY[0]]
+            res["lotus"] = run_lotus()
+            torch.cuda.empty_cache()
+            res["hbm_probe"] = {k: run_probe(k)["GBps"] for k in ("copy", "read")}
+            res["hbm_probe"]["how"] = ("torch copy_ (read + write) and max (read) of 1 GiB: "
+                                       "the bandwidth a library kernel reaches")
+    res["configs"] = configs
     res["page_manager"] = run_page_mgr()
     print(json.dumps(res), flush=True)
 

@@ -14,7 +14,16 @@
         HBM bytes per launch of the kernel whose name contains SUBSTR:
         FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by what the same
         counters read for a plain copy of N bytes (bytes read and written,
-        divided by the counter's reading).
+        divided by the counter's reading);
+    python -m paged_kv_attention_kvcache_amd.rocprof_summary workloads \\
+            --stats DIR --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
+            --copy-bytes N --json OUT
+        per bench.py workload (WORKLOAD_KERNELS): the average duration of
+        each kernel one call launches (kernel trace of a default bench.py
+        run), their sum per call, and the HBM bytes per call from the
+        counter runs, with the hash of the sources they were taken on;
+    python -m paged_kv_attention_kvcache_amd.rocprof_summary write OUT --profiles DIR
+        every committed summary, from the runs collect_profiles.sh leaves in OUT.
 """
 from __future__ import annotations
 
@@ -30,18 +39,28 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-# Sources the decode kernels are built from (the counter readings stored
-# for the decode workloads stay valid while these are unchanged).
-NOT_DECODE = ("prefill.hip", "prefill_mfma.hip", "prefill_cols.hip", "kv_write.hip")
+# The kernels one call of each bench.py workload launches, as (substring of
+# the kernel's name, grid size in threads or None for any): the dominant
+# kernel first, then the split-K combine where the split needs one.
+WORKLOAD_KERNELS = {
+    "ouro": [("decode_whole<pkv::BF16, pkv::ValuFold<pkv::BF16, 128, 2, false>", None)],
+    "huginn": [("decode_whole<pkv::BF16, pkv::ValuFold<pkv::BF16, 128, 1, false>", None)],
+    "longctx": [("decode_stream<pkv::BF16, pkv::MfmaFold<8, false>", None),
+                ("decode_stream_combine<pkv::BF16, 8>", None)],
+    "longctx_p512": [("decode_parts<pkv::BF16, pkv::MfmaFold<8, false>", None),
+                     ("decode_parts_combine<pkv::BF16, 8>", None)],
+    "prefill_cold2048": [("prefill_mfma", 131072)],
+    "prefill_8x2048": [("prefill_mfma", 524288)],
+}
 
 
 def kernel_source_hash() -> str:
-    """Hash of the decode kernels' sources (.hip, .hpp), to tie counter
-    readings to the kernels they were taken on."""
+    """Hash of the library's sources (.hip, .hpp, .cpp), to tie timings and
+    counter readings to the kernels they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")) and name not in NOT_DECODE:
+        if name.endswith((".hip", ".hpp", ".cpp")):
             h.update(name.encode())
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
@@ -129,6 +148,66 @@ def traffic(args) -> dict:
     return res
 
 
+def pmc_by_shape(d: str) -> dict:
+    """{(kernel short name, grid size): {counter: mean over dispatches}}."""
+    rows = csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv"))))
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in rows:
+        key = (short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+        acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def _match(name: str, grid: int, substr: str, want_grid) -> bool:
+    return substr in name and (want_grid is None or grid == want_grid)
+
+
+def workloads(stats_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir,
+              copy_bytes: float) -> dict:
+    """Per workload of WORKLOAD_KERNELS: kernel averages from a kernel trace
+    and HBM bytes per call from FETCH_SIZE / WRITE_SIZE runs, scaled by the
+    counters' reading for a plain copy of copy_bytes bytes."""
+    shapes = shape_stats(stats_dir)
+    cf = pmc_averages(copy_fetch_dir)
+    cw = pmc_averages(copy_write_dir)
+    fetch_scale = copy_bytes / (max(v.get("FETCH_SIZE", 0.0) for v in cf.values()) * 1024.0)
+    write_scale = copy_bytes / (max(v.get("WRITE_SIZE", 0.0) for v in cw.values()) * 1024.0)
+    fetch = pmc_by_shape(fetch_dir)
+    write = pmc_by_shape(write_dir)
+    out = {"kernel_source_hash": kernel_source_hash(), "fetch_scale": round(fetch_scale, 4),
+           "write_scale": round(write_scale, 4), "workloads": {}}
+    for wl, kernels in WORKLOAD_KERNELS.items():
+        ks, total_us, read_b, write_b, ok = [], 0.0, 0.0, 0.0, True
+        for substr, grid in kernels:
+            hits = [r for r in shapes if _match(r["name"], r["grid"][0], substr, grid)]
+            if not hits:
+                ok = False
+                break
+            calls = sum(r["calls"] for r in hits)
+            avg = sum(r["avg_us"] * r["calls"] for r in hits) / calls
+            f = [v["FETCH_SIZE"] for (n, g), v in fetch.items()
+                 if _match(n, g, substr, grid) and "FETCH_SIZE" in v]
+            w = [v["WRITE_SIZE"] for (n, g), v in write.items()
+                 if _match(n, g, substr, grid) and "WRITE_SIZE" in v]
+            rb = max(f) * 1024 * fetch_scale if f else None
+            wb = max(w) * 1024 * write_scale if w else None
+            ks.append({"kernel": hits[0]["name"], "grid": hits[0]["grid"][0], "calls": calls,
+                       "avg_us": round(avg, 3), "hbm_read_bytes": None if rb is None else round(rb),
+                       "hbm_write_bytes": None if wb is None else round(wb)})
+            total_us += avg
+            if rb is None or wb is None:
+                read_b = write_b = None
+            elif read_b is not None:
+                read_b += rb
+                write_b += wb
+        if not ok:
+            continue
+        out["workloads"][wl] = {
+            "kernels": ks, "us_per_call": round(total_us, 3),
+            "hbm_bytes_per_call": None if read_b is None else round(read_b + write_b)}
+    return out
+
+
 def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.4e9) -> list[dict]:
     """Per launch shape of the kernels matching `kernel`: the mean of each
     counter per dispatch and what follows from them. SQ_VALU_MFMA_BUSY_CYCLES
@@ -160,6 +239,103 @@ def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.
     return out
 
 
+COLLECT = "bash paged_kv_attention_kvcache_amd/collect_profiles.sh OUT"
+
+
+def _stats_text(d: str) -> str:
+    lines = [f"{'kernel':110s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+             f"{'%':>6s}"]
+    for r in kernel_stats(d):
+        if "pkv::" in r["name"]:
+            lines.append(f"{r['name']:110s} {r['calls']:6d} {r['avg_us']:10.2f} "
+                         f"{r['min_us']:10.2f} {r['max_us']:10.2f} {r['pct']:6.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def _shapes_text(d: str) -> str:
+    lines = [f"{'kernel':80s} {'grid (threads)':>15s} {'calls':>6s} {'avg_us':>10s} "
+             f"{'min_us':>10s} {'max_us':>10s}"]
+    for r in shape_stats(d):
+        if "pkv::" in r["name"]:
+            lines.append(f"{r['name'][:80]:80s} {r['grid'][0]:15d} {r['calls']:6d} "
+                         f"{r['avg_us']:10.2f} {r['min_us']:10.2f} {r['max_us']:10.2f}")
+    return "\n".join(lines) + "\n"
+
+
+def write_profiles(out: str, profiles: str) -> None:
+    """The committed summaries, from the runs of collect_profiles.sh in out."""
+    j = lambda name: os.path.join(out, name)
+    os.makedirs(profiles, exist_ok=True)
+    res = workloads(j("stats_default"), j("all_fetch"), j("all_write"), j("copy_fetch"),
+                    j("copy_write"), float(1 << 30))
+    res["produced_by"] = COLLECT
+    with open(os.path.join(profiles, "kernels.json"), "w") as fh:
+        fh.write(json.dumps(res, indent=1) + "\n")
+    h = res["kernel_source_hash"]
+    hdr = f"""# rocprofv3 kernel statistics of the default benchmark (python3 bench.py: the Ouro
+# headline step, then every other workload under "configs"), library sources {h}.
+# Produced from the repository root by {COLLECT}, whose run is
+#   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/stats_default -o run -- python3 bench.py
+# and summarised with
+#   python -m paged_kv_attention_kvcache_amd.rocprof_summary stats OUT/stats_default
+#   python -m paged_kv_attention_kvcache_amd.rocprof_summary shapes OUT/stats_default
+# Durations in microseconds; % = share of all GPU kernel time in the run (the rest is
+# the seeded input generation, done before each timed region).
+# Per kernel:
+"""
+    with open(os.path.join(profiles, "bench_default_kernel_stats.txt"), "w") as fh:
+        fh.write(hdr + _stats_text(j("stats_default")) +
+                 "\n# Per launch shape (grid in threads):\n" + _shapes_text(j("stats_default")))
+    hdr = f"""# HBM traffic and kernel time per call of each benchmark workload, library sources {h}.
+# Produced from the repository root by {COLLECT}, whose runs are
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/copy_fetch -o run -- python3 bench.py --probe copy
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/copy_write -o run -- python3 bench.py --probe copy
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/all_fetch -o run -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/all_write -o run -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
+# plus the kernel trace of bench_default_kernel_stats.txt, summarised with
+#   python -m paged_kv_attention_kvcache_amd.rocprof_summary workloads --stats OUT/stats_default --fetch OUT/all_fetch --write OUT/all_write --copy-fetch OUT/copy_fetch --copy-write OUT/copy_write --copy-bytes 1073741824 --json profiles/kernels.json
+# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; the plain copy of 1 GiB (1 GiB read and
+# written) reads fetch x {res['fetch_scale']} and write x {res['write_scale']}, the factors applied here.
+"""
+    lines = []
+    for wl, r in res["workloads"].items():
+        lines.append(f"{wl}: {r['us_per_call']:.2f} us per call, HBM bytes per call "
+                     f"{r['hbm_bytes_per_call']}")
+        for k in r["kernels"]:
+            lines.append(f"    {k['kernel']}  grid {k['grid']}  calls {k['calls']}  avg_us "
+                         f"{k['avg_us']:.2f}  read {k['hbm_read_bytes']}  write "
+                         f"{k['hbm_write_bytes']}")
+    with open(os.path.join(profiles, "hbm_traffic.txt"), "w") as fh:
+        fh.write(hdr + "\n".join(lines) + "\n")
+    counters = ("GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+                "SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES")
+    hdr = f"""# rocprofv3 engine counters of the prefill kernels per launch shape (grid in threads, 256
+# per workgroup), library sources {h}. Produced from the repository root by {COLLECT}:
+#   rocprofv3 --pmc {counters} --output-format csv -d OUT/prefill_engine -o run -- python3 bench.py --prefill-only --no-cpu-baseline
+#   python -m paged_kv_attention_kvcache_amd.rocprof_summary engine OUT/prefill_engine --kernel prefill
+# us: mean dispatch time under counter collection; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES /
+# (1024 SIMDs x 2.4 GHz x time); valu_per_mfma = SQ_INSTS_VALU / SQ_INSTS_MFMA.
+"""
+    body = []
+    for r in engine_counters(j("prefill_engine"), "prefill"):
+        body.append(f"{r['kernel']}  grid {r['grid']}  ({r['dispatches']} dispatches)")
+        for k, v in r.items():
+            if k not in ("kernel", "grid", "dispatches"):
+                body.append(f"    {k:28s} {v:.6g}")
+    with open(os.path.join(profiles, "prefill_engine_counters.txt"), "w") as fh:
+        fh.write(hdr + "\n".join(body) + "\n")
+    hdr = f"""# L2 hit rates per kernel and launch shape, library sources {h}: TCC_HIT / (TCC_HIT +
+# TCC_MISS) over the dies' L2 caches. Produced from the repository root by {COLLECT}:
+#   rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d OUT/all_l2 -o run -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline
+#   python -m paged_kv_attention_kvcache_amd.rocprof_summary engine OUT/all_l2 --kernel pkv::
+"""
+    body = [f"{r['kernel'][:80]:80s} grid {r['grid']:9d}  dispatches {r['dispatches']:5d}  "
+            f"l2_hit {r.get('l2_hit', float('nan')):.3f}"
+            for r in engine_counters(j("all_l2"), "pkv::")]
+    with open(os.path.join(profiles, "l2_hit_rates.txt"), "w") as fh:
+        fh.write(hdr + "\n".join(body) + "\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -178,6 +354,13 @@ def main(argv=None):
         t.add_argument(k, required=True)
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--json", default=None)
+    w = sub.add_parser("workloads")
+    for k in ("--stats", "--fetch", "--write", "--copy-fetch", "--copy-write", "--json"):
+        w.add_argument(k, required=True)
+    w.add_argument("--copy-bytes", type=float, required=True)
+    wr = sub.add_parser("write")
+    wr.add_argument("out")
+    wr.add_argument("--profiles", required=True)
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(f"{'kernel':110s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'%':>6s}")
@@ -204,6 +387,15 @@ def main(argv=None):
             for k, v in r.items():
                 if k not in ("kernel", "grid", "dispatches"):
                     print(f"    {k:28s} {v:.6g}")
+    elif args.cmd == "write":
+        write_profiles(args.out, args.profiles)
+    elif args.cmd == "workloads":
+        res = workloads(args.stats, args.fetch, args.write, args.copy_fetch, args.copy_write,
+                        args.copy_bytes)
+        text = json.dumps(res, indent=1)
+        print(text)
+        with open(args.json, "w") as fh:
+            fh.write(text + "\n")
     else:
         res = traffic(args)
         text = json.dumps(res, indent=1)

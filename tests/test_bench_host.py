@@ -21,15 +21,32 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_traffic_follows_the_source_hash(monkeypatch):
-    stored = json.load(open(os.path.join(ROOT, "profiles", "traffic_ouro.json")))
+def test_profiles_follow_the_source_hash(monkeypatch):
     from paged_kv_attention_kvcache_amd import rocprof_summary
 
-    if stored["kernel_source_hash"] == rocprof_summary.kernel_source_hash():
-        assert bench.traffic_from_profiles("ouro") == stored["hbm_bytes_per_launch"]
+    path = os.path.join(ROOT, "profiles", "kernels.json")
+    if os.path.exists(path):
+        stored = json.load(open(path))
+        if stored["kernel_source_hash"] == rocprof_summary.kernel_source_hash():
+            assert bench.profile_for("ouro") == stored["workloads"]["ouro"]
     monkeypatch.setattr(rocprof_summary, "kernel_source_hash", lambda: "0" * 16)
-    assert bench.traffic_from_profiles("ouro") is None
-    assert bench.traffic_from_profiles("no_such_workload") is None
+    assert bench.profile_for("ouro") is None
+    assert bench.profile_for("no_such_workload") is None
+
+
+def test_roofline_prices_the_call_both_ways(monkeypatch):
+    # 340 MB per call in 58 us live; the committed profile says 59 us and
+    # 343 MB of counter-measured HBM traffic
+    monkeypatch.setattr(bench, "profile_for", lambda w: {"us_per_call": 59.0,
+                                                         "hbm_bytes_per_call": 343_000_000})
+    r = bench.roofline("ouro", "k", 340e6 / 58e-6 / 1e9, 8000.0, "GB/s", "hbm", 340e6, 58e-6)
+    assert r["frac"] == round(340e6 / 58e-6 / 1e9 / 8000.0, 4)
+    assert r["traffic"] == 343_000_000 and r["profiled_us_per_call"] == 59.0
+    assert r["achieved_profiled"] == round(340e6 / 59e-6 / 1e9, 2)
+    assert r["hip_event_us_per_call"] == 58.0
+    monkeypatch.setattr(bench, "profile_for", lambda w: None)
+    r = bench.roofline("ouro", "k", 1.0, 8000.0, "GB/s", "hbm", 1.0, 1.0)
+    assert r["traffic"] is None and "achieved_profiled" not in r
 
 
 def test_workload_configs_name_the_shapes():

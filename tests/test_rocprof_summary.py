@@ -93,10 +93,61 @@ def test_engine_figures(tmp_path):
     assert rs.engine_counters(d, "prefill") == []
 
 
-def test_source_hash_covers_decode_sources_only():
+def test_source_hash_covers_every_library_source(tmp_path, monkeypatch):
     h = rs.kernel_source_hash()
     assert len(h) == 16 and h == rs.kernel_source_hash()
-    names = sorted(n for n in os.listdir(os.path.join(rs.HERE, "csrc"))
-                   if n.endswith((".hip", ".hpp")))
-    assert "decode.hip" in names and "prefill_mfma.hip" in names
-    assert set(rs.NOT_DECODE) <= set(names)
+    # a change to any source (a prefill kernel, the host code) changes the hash
+    import shutil
+
+    fake = tmp_path / "pkg"
+    shutil.copytree(os.path.join(rs.HERE, "csrc"), fake / "csrc")
+    monkeypatch.setattr(rs, "HERE", str(fake))
+    assert rs.kernel_source_hash() == h
+    for name in ("prefill_mfma.hip", "pagedkv.cpp", "span.hpp"):
+        p = fake / "csrc" / name
+        old = p.read_text()
+        p.write_text(old + "\n")
+        assert rs.kernel_source_hash() != h, name
+        p.write_text(old)
+
+
+def test_workload_figures(tmp_path):
+    # Two workloads in one trace: the long-context call (stream kernel 3200 us
+    # + combine 13 us) and the 8 x 2048 prefill (grid 524288; the 131072-grid
+    # prefill calls belong to another workload). Copy probe: scales 2 and 1.
+    base = str(tmp_path)
+    stream = "void pkv::decode_stream<pkv::BF16, pkv::MfmaFold<8, false> >(uint4 const*)"
+    comb = "void pkv::decode_stream_combine<pkv::BF16, 8>(int)"
+    pre = "void pkv::prefill_mfma<4, 2, 2048>(uint4 const*)"
+    st = os.path.join(base, "st")
+    os.makedirs(st)
+    _write(os.path.join(st, "run_kernel_trace.csv"),
+           ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+            "End_Timestamp"],
+           [[stream, 262144, 1, 1, 0, 3200000], [stream, 262144, 1, 1, 0, 3210000],
+            [comb, 524288, 1, 1, 0, 13000], [pre, 524288, 1, 1, 0, 330000],
+            [pre, 131072, 1, 1, 0, 39000]])
+    _counters(os.path.join(base, "cf"), [[1, 256, COPY, "FETCH_SIZE", 512.0, 0, 10]])
+    _counters(os.path.join(base, "cw"), [[1, 256, COPY, "WRITE_SIZE", 1024.0, 0, 10]])
+    _counters(os.path.join(base, "kf"), [[1, 262144, stream, "FETCH_SIZE", 1000.0, 0, 10],
+                                         [2, 524288, comb, "FETCH_SIZE", 10.0, 0, 10],
+                                         [3, 524288, pre, "FETCH_SIZE", 300.0, 0, 10],
+                                         [4, 131072, pre, "FETCH_SIZE", 99.0, 0, 10]])
+    _counters(os.path.join(base, "kw"), [[1, 262144, stream, "WRITE_SIZE", 4.0, 0, 10],
+                                         [2, 524288, comb, "WRITE_SIZE", 2.0, 0, 10],
+                                         [3, 524288, pre, "WRITE_SIZE", 100.0, 0, 10],
+                                         [4, 131072, pre, "WRITE_SIZE", 9.0, 0, 10]])
+    out = os.path.join(base, "w.json")
+    rs.main(["workloads", "--stats", st, "--fetch", os.path.join(base, "kf"),
+             "--write", os.path.join(base, "kw"), "--copy-fetch", os.path.join(base, "cf"),
+             "--copy-write", os.path.join(base, "cw"), "--copy-bytes", str(1 << 20),
+             "--json", out])
+    res = json.load(open(out))
+    assert res["kernel_source_hash"] == rs.kernel_source_hash()
+    w = res["workloads"]
+    assert set(w) == {"longctx", "prefill_8x2048", "prefill_cold2048"}
+    assert w["longctx"]["us_per_call"] == pytest.approx(3205.0 + 13.0)
+    assert w["longctx"]["hbm_bytes_per_call"] == (1010 * 2 + 6) * 1024
+    assert w["prefill_8x2048"]["us_per_call"] == pytest.approx(330.0)
+    assert w["prefill_8x2048"]["hbm_bytes_per_call"] == (300 * 2 + 100) * 1024
+    assert w["prefill_cold2048"]["us_per_call"] == pytest.approx(39.0)
