@@ -130,4 +130,17 @@ __device__ __forceinline__ uint4 load_stream(const void *p) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// A 16-byte K/V load: non-temporal (load_stream) for pages one request
+// reads, or an ordinary cached load (C) for pages other requests of the call
+// read too, so that they find them in L2. The policy is a compile-time
+// choice: each loop streams with one kind of load.
+template <bool C>
+__device__ __forceinline__ uint4 load_kv(const void *p) {
+  if constexpr (C) {
+    return *reinterpret_cast<const uint4 *>(p);
+  } else {
+    return load_stream(p);
+  }
+}
+
 }  // namespace pkv

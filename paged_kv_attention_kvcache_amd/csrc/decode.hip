@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * W) void decode_whole(
     const int32_t *__restrict__ seq_lens, int32_t batch, int32_t max_seq_len, float qscale,
     typename E::storage *__restrict__ out, float *__restrict__ lse,
     const typename E::storage *__restrict__ k_new, const typename E::storage *__restrict__ v_new,
-    uint4 *kb_w, uint4 *vb_w, LatestArgs la) {
+    uint4 *kb_w, uint4 *vb_w, LatestArgs la, int32_t pair) {
   constexpr int G = F::kGroup, D = F::kHeadDim;
   constexpr int kThreads = 64 * W;
   __shared__ float2 lds_ml[W * G];
@@ -155,18 +155,35 @@ __global__ __launch_bounds__(64 * W) void decode_whole(
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Lane i < batch: the clamped length of request i and its rank in
-  // longest-first order (ties by index).
+  // longest-first order (ties by index); and whether its first page is also
+  // another request's first page (a shared prefix: its pages are then read
+  // with cached loads, so that the other requests find them in L2).
   const int mine = lane < batch ? min(max(seq_lens[lane], 0), max_seq_len) : -1;
+  const int first = mine > 0 ? page_table[(size_t)lane * pt_stride] : -1 - lane;
   int rank = 0;
+  bool shared = false;
   for (int j = 0; j < batch; ++j) {
     const int o = __builtin_amdgcn_readlane(mine, j);
     rank += (o > mine) || (o == mine && j < lane);
+    shared |= j != lane && __builtin_amdgcn_readlane(first, j) == first;
   }
   const int units = batch * hkv, M = gridDim.x, k = blockIdx.x;
   for (int it = 0;; ++it) {
     const int base = 2 * M * (it >> 1);
-    const int u = (it & 1) ? base + 2 * M - 1 - k : base + k;
-    if (u >= units) break;  // ranks grow with it
+    int u = (it & 1) ? base + 2 * M - 1 - k : base + k;
+    // With two workgroups per compute unit (pair: M = 2 x CUs), workgroups
+    // k and k + M/2 share one; the second half takes its first units in
+    // reverse order (in steps of 8, keeping u % 8 = k % 8, the die of
+    // workgroup k), so a long context shares its compute unit with a short
+    // one and soon has it alone.
+    if (pair && it == 0 && k >= M / 2) {
+      const int j = k - M / 2;
+      u = M / 2 + (M / 2 - 8 - (j & ~7)) + (j & 7);
+    }
+    if (u >= units) {
+      if (it == 0) continue;  // a permuted first unit may be past the end
+      break;  // ranks grow with it
+    }
     const int kvh = u % hkv;
     const unsigned long long hit = __ballot(lane < batch && rank == u / hkv);
     const int r = hit ? __ffsll(hit) - 1 : 0;
@@ -185,9 +202,19 @@ __global__ __launch_bounds__(64 * W) void decode_whole(
         f.set_append(k_new + ((size_t)r * hkv + kvh) * D, v_new + ((size_t)r * hkv + kvh) * D,
                      n - 1, kb_w, vb_w, min(max(pt_row[pa], 0), num_pages - 1), hkv, kvh);
     }
-    if (npw > 0)
-      stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, w, npw, W, 0, n,
-                   F::kLatest ? la.depth + (size_t)r * la.stride : nullptr);
+    if (npw > 0) {
+      const uint8_t *ex_row = F::kLatest ? la.depth + (size_t)r * la.stride : nullptr;
+      bool done = false;
+      if constexpr (!F::kLatest && F::kGroup == 1) {
+        if (__builtin_amdgcn_readlane((int)shared, r)) {
+          stream_pages<F, NoStepHook, true>(f, st, kb, vb, pt_row, num_pages, hkv, kvh, w, npw,
+                                            W, 0, n, ex_row);
+          done = true;
+        }
+      }
+      if (!done)
+        stream_pages(f, st, kb, vb, pt_row, num_pages, hkv, kvh, w, npw, W, 0, n, ex_row);
+    }
     f.finish_wave(st);
     emit_to_lds(f, st, w, lds_ml, lds_acc);
     __syncthreads();
@@ -244,6 +271,7 @@ static hipError_t decode_fold(const DecodeArgs &a, hipStream_t stream) {
     }
     const int units = a.batch * a.bank.num_kv_heads;
     const int blocks = std::min(units, a.num_cus * per_cu);
+    const int pair = blocks == 2 * a.num_cus && a.num_cus % 8 == 0 ? 1 : 0;
     hipLaunchKernelGGL((decode_whole<E, F, W>), dim3(blocks), dim3(64 * W), 0, stream,
                        static_cast<const uint4 *>(a.bank.k), static_cast<const uint4 *>(a.bank.v),
                        a.bank.num_pages, a.bank.num_kv_heads,
@@ -253,7 +281,7 @@ static hipError_t decode_fold(const DecodeArgs &a, hipStream_t stream) {
                        static_cast<const typename E::storage *>(a.k_new),
                        static_cast<const typename E::storage *>(a.v_new),
                        static_cast<uint4 *>(a.bank.k), static_cast<uint4 *>(a.bank.v),
-                       a.latest);
+                       a.latest, pair);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((decode_block<E, F, W>), grid, dim3(64 * W), 0, stream,

@@ -130,6 +130,7 @@ struct MfmaFold {
     st.l = 0.f;
   }
 
+  template <bool C = false>
   __device__ __forceinline__ void load(Regs &r, const uint4 *__restrict__ kb,
                                        const uint4 *__restrict__ vb, int page0, int page1,
                                        int hkv, int kvh) const {
@@ -139,13 +140,13 @@ struct MfmaFold {
     const char *v0 = reinterpret_cast<const char *>(vb + t0);
     const char *v1 = reinterpret_cast<const char *>(vb + t1);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r.k[0][c] = load_stream(k0 + koff + c * 64);
+    for (int c = 0; c < 4; ++c) r.k[0][c] = load_kv<C>(k0 + koff + c * 64);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r.k[1][c] = load_stream(k1 + koff + c * 64);
+    for (int c = 0; c < 4; ++c) r.k[1][c] = load_kv<C>(k1 + koff + c * 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[0][i] = load_stream(v0 + voff + i * 256);
+    for (int i = 0; i < 4; ++i) r.v[0][i] = load_kv<C>(v0 + voff + i * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[1][i] = load_stream(v1 + voff + i * 256);
+    for (int i = 0; i < 4; ++i) r.v[1][i] = load_kv<C>(v1 + voff + i * 256);
   }
 
   // Folds pages piA and piB (piB = -1: absent) of the request; keys outside

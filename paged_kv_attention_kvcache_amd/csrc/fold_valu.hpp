@@ -37,6 +37,7 @@ struct ValuFold {
   static constexpr int kDepth = 2;  // steps in flight per wave (3 measured slower)
   static constexpr int kGroup = G;
   static constexpr int kHeadDim = D;
+  static constexpr float kLazy = 8.f;  // rescale threshold, log2 units
 
   struct State {
     float m[G], l[G], acc[G][N];
@@ -98,6 +99,7 @@ struct ValuFold {
 
   // The (page, kv head) tile rows this lane owns; page and kvh are
   // wave-uniform, so the tile base is a scalar address.
+  template <bool C = false>
   __device__ __forceinline__ void load(Regs &r, const uint4 *__restrict__ kb,
                                        const uint4 *__restrict__ vb, int page, int,
                                        int hkv, int kvh) const {
@@ -105,9 +107,9 @@ struct ValuFold {
     const char *kt = reinterpret_cast<const char *>(kb + tile);
     const char *vt = reinterpret_cast<const char *>(vb + tile);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) r.k[i] = load_stream(kt + lane_off + i * RPW * LPT * 16u);
+    for (int i = 0; i < NI; ++i) r.k[i] = load_kv<C>(kt + lane_off + i * RPW * LPT * 16u);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) r.v[i] = load_stream(vt + lane_off + i * RPW * LPT * 16u);
+    for (int i = 0; i < NI; ++i) r.v[i] = load_kv<C>(vt + lane_off + i * RPW * LPT * 16u);
   }
 
   // Early-exit variant of load: `ex` holds the 16 exit depths of the page's
@@ -154,14 +156,12 @@ struct ValuFold {
 
   __device__ __forceinline__ void fold_regs(State &st, const Regs &r, int pi, int lo,
                                             int hi) const {
-    auto kk = [&](int i) { return r.k[i]; };
-    auto vv = [&](int i) { return r.v[i]; };
     const int pos0 = pi * kPage + row;  // token of load i: pos0 + i * RPW
     const bool full = (pi * kPage >= lo) && (pi * kPage + kPage <= hi);
     float s[G][NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint4 k = kk(i);
+      const uint4 k = r.k[i];
 #pragma unroll
       for (int g = 0; g < G; ++g) s[g][i] = q[g].dot(k);
     }
@@ -179,36 +179,84 @@ struct ValuFold {
         for (int g = 0; g < G; ++g) s[g][i] = -INFINITY;
       }
     }
-    // One rescale per page and head, then the V rows one at a time (a masked
-    // row is replaced by zeros so that poison in unused slots cannot leak).
-    float ms[G];
+    // Each row state keeps a reference max m; it moves (and l, acc are
+    // rescaled) only when a score exceeds it by more than 2^kLazy, so the
+    // weights exp2(s - m) stay at most 2^kLazy (exact in fp32 and within
+    // bf16's range) and most pages skip the rescale. The branch is taken by
+    // the whole wave when any of its rows needs it.
+    float mx[G];
+    bool grow = false;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mx = s[g][0];
+      mx[g] = s[g][0];
 #pragma unroll
-      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[g][i]);
-      const float mn = fmaxf(st.m[g], mx);
-      ms[g] = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(st.m[g] - ms[g]);
-      st.l[g] *= alpha;
-#pragma unroll
-      for (int e = 0; e < N; ++e) st.acc[g][e] *= alpha;
-      st.m[g] = mn;
+      for (int i = 1; i < NI; ++i) mx[g] = fmaxf(mx[g], s[g][i]);
+      grow |= mx[g] > st.m[g] + kLazy;
     }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float vf[N];
-      Vec<E>::widen(vv(i), vf);
-      if (!valid[i]) {
-#pragma unroll
-        for (int e = 0; e < N; ++e) vf[e] = 0.f;
-      }
+    if (__any(grow)) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float p = fast_exp2(s[g][i] - ms[g]);
-        st.l[g] += p;
+        const float mn = fmaxf(st.m[g], mx[g]);
+        const float alpha = fast_exp2(st.m[g] - ((mn == -INFINITY) ? 0.f : mn));
+        st.l[g] *= alpha;
 #pragma unroll
-        for (int e = 0; e < N; ++e) st.acc[g][e] = fmaf(p, vf[e], st.acc[g][e]);
+        for (int e = 0; e < N; ++e) st.acc[g][e] *= alpha;
+        st.m[g] = mn;
+      }
+    }
+    float p[G][NI];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float nm = (st.m[g] == -INFINITY) ? 0.f : -st.m[g];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        p[g][i] = fast_exp2(s[g][i] + nm);
+        st.l[g] += p[g][i];  // the denominator sums the fp32 weights
+      }
+    }
+    if constexpr (N == 8) {
+      // bf16: V of two token rows interleaved per dim (v_perm_b32) meets the
+      // weights of those rows rounded to bf16 in one v_dot2_f32_bf16 (fp32
+      // accumulation). Rows outside [lo, hi) contribute exact zeros, so
+      // poison in unused slots cannot leak.
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      uint4 v[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) v[i] = valid[i] ? r.v[i] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        const uint32_t a[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        const uint32_t b[4] = {v[i + 1].x, v[i + 1].y, v[i + 1].z, v[i + 1].w};
+        uint32_t pp[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pp[g] = pack_bf16x2(p[g][i], p[g][i + 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo16 = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+          const uint32_t hi16 = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const bf16x2 w = __builtin_bit_cast(bf16x2, pp[g]);
+            st.acc[g][2 * j] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2, lo16), w, st.acc[g][2 * j], false);
+            st.acc[g][2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                __builtin_bit_cast(bf16x2, hi16), w, st.acc[g][2 * j + 1], false);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float vf[N];
+        Vec<E>::widen(r.v[i], vf);
+        if (!valid[i]) {
+#pragma unroll
+          for (int e = 0; e < N; ++e) vf[e] = 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < N; ++e) st.acc[g][e] = fmaf(p[g][i], vf[e], st.acc[g][e]);
       }
     }
   }

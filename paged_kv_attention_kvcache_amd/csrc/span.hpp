@@ -28,8 +28,9 @@ struct NoStepHook {
 // Streams `count` pages p_first + stride * k (k = 0 .. count-1) of one
 // (request, kv head) through fold f; keys outside [lo, hi) are masked. After
 // each step, after(k) runs with k = the pages folded so far (a multiple of
-// F::kPagesPerStep, or count); it may hand the state on and reset it.
-template <class F, class After = NoStepHook>
+// F::kPagesPerStep, or count); it may hand the state on and reset it. C:
+// cached K/V loads (pages other requests read too) instead of non-temporal.
+template <class F, class After = NoStepHook, bool C = false>
 __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
                                              const uint4 *__restrict__ kb,
                                              const uint4 *__restrict__ vb,
@@ -64,7 +65,7 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
                                    __builtin_amdgcn_readlane(ex.w, k));
         f.load_latest(r, kb, vb, page(s), e, hkv, kvh);
       } else {
-        f.load(r, kb, vb, page(s * S), page(s * S + S - 1), hkv, kvh);
+        f.template load<C>(r, kb, vb, page(s * S), page(s * S + S - 1), hkv, kvh);
       }
     };
     // A fold ends with a compiler-only barrier: the next load into the same
