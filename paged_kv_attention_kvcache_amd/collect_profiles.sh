@@ -34,5 +34,13 @@ pmc all_write WRITE_SIZE python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-bas
 pmc prefill_engine "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES" \
   python3 "$R/bench.py" --prefill-only --no-cpu-baseline
 pmc all_l2 "TCC_HIT_sum TCC_MISS_sum" python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-baseline
+# What bounds the decode kernels: L1->L2 and L2->memory read latency, TLB
+# misses, instruction counts and waits (decode workloads only).
+pmc decode_tcp "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_REQUEST_sum" \
+  python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-baseline --no-prefill
+pmc decode_tcc "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum" \
+  python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-baseline --no-prefill
+pmc decode_sq "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INST_LEVEL_VMEM SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_BUSY_CYCLES SQ_WAVES" \
+  python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-baseline --no-prefill
 echo "== summaries $(date +%T)"
 python3 -m paged_kv_attention_kvcache_amd.rocprof_summary write "$OUT" --profiles "$R/profiles"

@@ -334,6 +334,55 @@ def write_profiles(out: str, profiles: str) -> None:
             for r in engine_counters(j("all_l2"), "pkv::")]
     with open(os.path.join(profiles, "l2_hit_rates.txt"), "w") as fh:
         fh.write(hdr + "\n".join(body) + "\n")
+    hdr = f"""# Memory-pipeline counters of the decode kernels per launch shape, library sources {h}.
+# Produced from the repository root by {COLLECT}, whose runs are (one counter set each)
+#   rocprofv3 --pmc TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_REQUEST_sum --output-format csv -d OUT/decode_tcp -o run -- python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-prefill
+#   rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum --output-format csv -d OUT/decode_tcc -o run -- (the same)
+#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INST_LEVEL_VMEM SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_BUSY_CYCLES SQ_WAVES --output-format csv -d OUT/decode_sq -o run -- (the same)
+# l1_to_l2_latency_clk = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (average clocks from an L1
+# miss to its L2 data); l2_to_mem_latency_clk = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ (average
+# clocks an L2 read to the memory side is outstanding); counts are per dispatch. Kernel names
+# separate the workloads: ValuFold<BF16, 128, 2> is the Ouro shape, ValuFold<BF16, 128, 1> the
+# Huginn shape, MfmaFold<8> the long-context shape (balanced split and fixed partitions).
+"""
+    body = []
+    for d in decode_memory(out):
+        body.append(f"{d['kernel']}  grid {d['grid']}")
+        for k, v in d.items():
+            if k not in ("kernel", "grid") and v is not None:
+                body.append(f"    {k:24s} {v:.6g}")
+    with open(os.path.join(profiles, "decode_memory_counters.txt"), "w") as fh:
+        fh.write(hdr + "\n".join(body) + "\n")
+
+
+def decode_memory(out: str) -> list[dict]:
+    """Per decode kernel and launch shape, from the decode_tcp / decode_tcc /
+    decode_sq runs: the average L1->L2 read latency (TCP_TCC_READ_REQ_LATENCY
+    / TCP_TCC_READ_REQ, clocks), the average L2->memory read latency
+    (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ, clocks), the L2 hit rate, TLB
+    misses per dispatch, and VALU and vector-load instructions per dispatch."""
+    rows = {}
+    for run in ("decode_tcp", "decode_tcc", "decode_sq"):
+        for r in engine_counters(os.path.join(out, run), "decode"):
+            rows.setdefault((r["kernel"], r["grid"]), {}).update(r)
+    res = []
+    for (k, g), r in sorted(rows.items()):
+        d = {"kernel": k, "grid": g, "us": r.get("us")}
+        if r.get("TCP_TCC_READ_REQ_sum"):
+            d["l1_to_l2_latency_clk"] = r["TCP_TCC_READ_REQ_LATENCY_sum"] / r["TCP_TCC_READ_REQ_sum"]
+            d["l2_read_requests"] = r["TCP_TCC_READ_REQ_sum"]
+        if "TCP_UTCL1_TRANSLATION_MISS_sum" in r:
+            d["tlb_misses"] = r["TCP_UTCL1_TRANSLATION_MISS_sum"]
+        if r.get("TCC_EA0_RDREQ_sum"):
+            d["l2_to_mem_latency_clk"] = r["TCC_EA0_RDREQ_LEVEL_sum"] / r["TCC_EA0_RDREQ_sum"]
+        if "l2_hit" in r:
+            d["l2_hit"] = r["l2_hit"]
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                  "SQ_WAVE_CYCLES", "SQ_WAVES"):
+            if c in r:
+                d[c] = r[c]
+        res.append(d)
+    return res
 
 
 def main(argv=None):

@@ -151,3 +151,52 @@ def test_workload_figures(tmp_path):
     assert w["prefill_8x2048"]["us_per_call"] == pytest.approx(330.0)
     assert w["prefill_8x2048"]["hbm_bytes_per_call"] == (300 * 2 + 100) * 1024
     assert w["prefill_cold2048"]["us_per_call"] == pytest.approx(39.0)
+
+
+def test_write_profiles_from_a_collection(tmp_path):
+    # every summary collect_profiles.sh asks for, from minimal runs of each kind
+    out = tmp_path / "out"
+    ouro = "void pkv::decode_whole<pkv::BF16, pkv::ValuFold<pkv::BF16, 128, 2, false>, 8>(int)"
+    pre = "void pkv::prefill_mfma<4, 2, 2048>(uint4 const*)"
+    st = out / "stats_default"
+    st.mkdir(parents=True)
+    _write(str(st / "run_kernel_stats.csv"),
+           ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+           [[ouro, 2, 120000, 60000, 50.0, 59000, 61000], [pre, 1, 330000, 330000, 50.0,
+                                                           330000, 330000]])
+    _write(str(st / "run_kernel_trace.csv"),
+           ["Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+            "End_Timestamp"],
+           [[ouro, 131072, 1, 1, 0, 59000], [ouro, 131072, 1, 1, 0, 61000],
+            [pre, 524288, 1, 1, 0, 330000]])
+    _counters(str(out / "copy_fetch"), [[1, 256, COPY, "FETCH_SIZE", 512.0, 0, 10]])
+    _counters(str(out / "copy_write"), [[1, 256, COPY, "WRITE_SIZE", 1024.0, 0, 10]])
+    _counters(str(out / "all_fetch"), [[1, 131072, ouro, "FETCH_SIZE", 100.0, 0, 10],
+                                      [2, 524288, pre, "FETCH_SIZE", 300.0, 0, 10]])
+    _counters(str(out / "all_write"), [[1, 131072, ouro, "WRITE_SIZE", 1.0, 0, 10],
+                                      [2, 524288, pre, "WRITE_SIZE", 100.0, 0, 10]])
+    _counters(str(out / "prefill_engine"), [[1, 524288, pre, "SQ_VALU_MFMA_BUSY_CYCLES", 1e6,
+                                             0, 100000]])
+    _counters(str(out / "all_l2"), [[1, 131072, ouro, "TCC_HIT_sum", 10.0, 0, 10],
+                                   [1, 131072, ouro, "TCC_MISS_sum", 90.0, 0, 10]])
+    _counters(str(out / "decode_tcp"), [[1, 131072, ouro, "TCP_TCC_READ_REQ_LATENCY_sum", 5000.0,
+                                         0, 10],
+                                        [1, 131072, ouro, "TCP_TCC_READ_REQ_sum", 10.0, 0, 10]])
+    _counters(str(out / "decode_tcc"), [[1, 131072, ouro, "TCC_EA0_RDREQ_LEVEL_sum", 1400.0, 0, 10],
+                                        [1, 131072, ouro, "TCC_EA0_RDREQ_sum", 1.0, 0, 10]])
+    _counters(str(out / "decode_sq"), [[1, 131072, ouro, "SQ_INSTS_VALU", 7.0, 0, 10]])
+    prof = tmp_path / "profiles"
+    rs.main(["write", str(out), "--profiles", str(prof)])
+    names = sorted(os.listdir(prof))
+    assert names == ["bench_default_kernel_stats.txt", "decode_memory_counters.txt",
+                     "hbm_traffic.txt", "kernels.json", "l2_hit_rates.txt",
+                     "prefill_engine_counters.txt"]
+    k = json.load(open(prof / "kernels.json"))
+    assert k["workloads"]["ouro"]["us_per_call"] == pytest.approx(60.0)
+    # the copy probe of 1 GiB read 512 KiB of FETCH_SIZE and 1024 KiB of WRITE_SIZE
+    assert k["workloads"]["prefill_8x2048"]["hbm_bytes_per_call"] == \
+        300 * 1024 * 2048 + 100 * 1024 * 1024
+    text = (prof / "decode_memory_counters.txt").read_text()
+    assert "l1_to_l2_latency_clk     500" in text and "l2_to_mem_latency_clk    1400" in text
+    for n in names:
+        assert "collect_profiles.sh" in (prof / n).read_text()
