@@ -23,7 +23,8 @@
 // (32 KiB) are copied from HBM straight into LDS with global_load_lds_dwordx4
 // (no register staging), into a ring of stages: with two stages (two
 // workgroups per CU) the next step is in flight while one is folded, with
-// four (one workgroup per CU, longer contexts) the next three are. Each wave waits for its own copies with an
+// three or four (one workgroup per CU, longer contexts) the next two or three
+// are. Each wave waits for its own copies with an
 // explicit vmcnt and one barrier per step publishes the stage (the compiler
 // does not track these copies, so the waits are written out). Within a
 // 256-byte token row the 16-byte chunk c of token t sits at c ^ t in a K
@@ -424,13 +425,15 @@ __global__ __launch_bounds__(kBlock) void prefill_mfma(
 }
 
 namespace {
-// One workgroup per CU: four 64-key stages (128 KiB) and page ids for 64k
-// tokens. Two per CU: two 64-key stages and page ids for 32k tokens.
-constexpr int kWideMaxPages = 4096, kNarrowMaxPages = 2048;
+// Two workgroups per CU: two 64-key stages (64 KiB) and page ids for 32k
+// tokens each. One per CU: four stages (128 KiB) and page ids for 64k
+// tokens, or three stages (96 KiB) and page ids for 256k tokens (64 KiB;
+// 160 KiB in all, the whole LDS of a CU).
+constexpr int kNarrowMaxPages = 2048, kWideMaxPages = 4096, kDeepMaxPages = 16384;
 }  // namespace
 
 bool prefill_mfma_supported(const PrefillArgs &a) {
-  return a.bank.dtype == 1 && a.bank.head_dim == 128 && a.max_seq_len <= kWideMaxPages * kPage;
+  return a.bank.dtype == 1 && a.bank.head_dim == 128 && a.max_seq_len <= kDeepMaxPages * kPage;
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
@@ -449,10 +452,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     return hipGetLastError();
   };
   // Two workgroups per CU (72 KiB of LDS each) hide one another's copy
-  // waits and softmax; the four-stage single-workgroup kernel covers longer
-  // contexts.
+  // waits and softmax; the single-workgroup kernels cover longer contexts.
   if (a.max_seq_len <= kNarrowMaxPages * kPage) return go(prefill_mfma<4, 2, kNarrowMaxPages>);
-  return go(prefill_mfma<4, 4, kWideMaxPages>);
+  if (a.max_seq_len <= kWideMaxPages * kPage) return go(prefill_mfma<4, 4, kWideMaxPages>);
+  return go(prefill_mfma<4, 3, kDeepMaxPages>);
 }
 
 }  // namespace pkv

@@ -393,7 +393,7 @@ def test_prefill_full_size_every_prompt():
                                         ([70000], [69900])])
 def test_prefill_long_context(lens, start):
     # suffixes over long cached prefixes: contexts past 32k tokens take the
-    # four-stage matrix-core kernel, past 64k tokens the vector-ALU kernel
+    # four-stage matrix-core kernel, past 64k tokens the three-stage one
     say(f"prefill long context {lens}")
     case = synth.make_prefill_case(6, "bf16", lens, 4, 2, 128)
     gp, op = gpu_pool(case.layout), oracle_pool(case.layout)
