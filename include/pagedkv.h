@@ -230,8 +230,8 @@ int paged_decode_append_attn(const pkv_pool *pool, int32_t plane_id, int32_t lay
  * enqueued otherwise): exit_depth 16-byte aligned; exit_stride a multiple of
  * 16 and >= max_seq_len; every plane 0..plane_id holds layer_id
  * (PKV_ENOTHELD), with the banks of planes 1..plane_id evenly spaced (true of
- * every pkv_bank_map layout; PKV_EUNSUPPORTED otherwise); GQA group 1 or 2
- * (PKV_EUNSUPPORTED otherwise). Device depths are not validated: a depth
+ * every pkv_bank_map layout; PKV_EUNSUPPORTED otherwise); GQA groups as for
+ * paged_decode_attn (1, 2, 4, 8). Device depths are not validated: a depth
  * at or past plane_id (or negative) reads plane_id's own bank. */
 int paged_decode_latest_attn(const pkv_pool *pool, int32_t plane_id, int32_t layer_id,
                              const int8_t *exit_depth, int32_t exit_stride, const void *k_new,

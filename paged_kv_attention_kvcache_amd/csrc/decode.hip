@@ -302,10 +302,12 @@ static hipError_t decode_fold(const DecodeArgs &a, hipStream_t stream) {
 
 template <typename E, int D>
 static hipError_t decode_by_group(const DecodeArgs &a, hipStream_t stream) {
-  if (a.latest.depth) {  // early exit: vector folds of groups 1 and 2
+  if (a.latest.depth) {  // early exit
     switch (a.num_q_heads / a.bank.num_kv_heads) {
-      case 1: return decode_fold<E, ValuFold<E, D, 1, true>>(a, stream);
-      case 2: return decode_fold<E, ValuFold<E, D, 2, true>>(a, stream);
+      case 1: return decode_fold<E, typename FoldFor<E, D, 1, true>::type>(a, stream);
+      case 2: return decode_fold<E, typename FoldFor<E, D, 2, true>::type>(a, stream);
+      case 4: return decode_fold<E, typename FoldFor<E, D, 4, true>::type>(a, stream);
+      case 8: return decode_fold<E, typename FoldFor<E, D, 8, true>::type>(a, stream);
     }
     return hipErrorInvalidValue;
   }

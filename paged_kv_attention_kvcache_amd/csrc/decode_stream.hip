@@ -483,8 +483,10 @@ template <typename E, int D>
 static hipError_t parts_by_group(const DecodeArgs &a, hipStream_t stream) {
   if (a.latest.depth) {
     switch (a.num_q_heads / a.bank.num_kv_heads) {
-      case 1: return parts_launch<E, ValuFold<E, D, 1, true>>(a, stream);
-      case 2: return parts_launch<E, ValuFold<E, D, 2, true>>(a, stream);
+      case 1: return parts_launch<E, typename FoldFor<E, D, 1, true>::type>(a, stream);
+      case 2: return parts_launch<E, typename FoldFor<E, D, 2, true>::type>(a, stream);
+      case 4: return parts_launch<E, typename FoldFor<E, D, 4, true>::type>(a, stream);
+      case 8: return parts_launch<E, typename FoldFor<E, D, 8, true>::type>(a, stream);
     }
     return hipErrorInvalidValue;
   }
@@ -497,16 +499,19 @@ static hipError_t parts_by_group(const DecodeArgs &a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-template <typename E, int D>
-static int pages_per_step(int group, bool latest) {
-  if (latest) return 1;
+template <typename E, int D, bool L>
+static int pages_per_step(int group) {
   switch (group) {
-    case 1: return FoldFor<E, D, 1>::type::kPagesPerStep;
-    case 2: return FoldFor<E, D, 2>::type::kPagesPerStep;
-    case 4: return FoldFor<E, D, 4>::type::kPagesPerStep;
-    case 8: return FoldFor<E, D, 8>::type::kPagesPerStep;
+    case 1: return FoldFor<E, D, 1, L>::type::kPagesPerStep;
+    case 2: return FoldFor<E, D, 2, L>::type::kPagesPerStep;
+    case 4: return FoldFor<E, D, 4, L>::type::kPagesPerStep;
+    case 8: return FoldFor<E, D, 8, L>::type::kPagesPerStep;
   }
   return 0;
+}
+template <typename E, int D>
+static int pages_per_step(int group, bool latest) {
+  return latest ? pages_per_step<E, D, true>(group) : pages_per_step<E, D, false>(group);
 }
 
 bool decode_parts_supported(const DecodeArgs &a) {
@@ -531,10 +536,12 @@ hipError_t launch_decode_parts(const DecodeArgs &a, hipStream_t stream) {
 
 template <typename E, int D>
 static hipError_t stream_by_group(const DecodeArgs &a, int64_t nw, hipStream_t stream) {
-  if (a.latest.depth) {  // early exit: vector folds of groups 1 and 2
+  if (a.latest.depth) {  // early exit
     switch (a.num_q_heads / a.bank.num_kv_heads) {
-      case 1: return stream_launch<E, D, 1, ValuFold<E, D, 1, true>>(a, nw, stream);
-      case 2: return stream_launch<E, D, 2, ValuFold<E, D, 2, true>>(a, nw, stream);
+      case 1: return stream_launch<E, D, 1, typename FoldFor<E, D, 1, true>::type>(a, nw, stream);
+      case 2: return stream_launch<E, D, 2, typename FoldFor<E, D, 2, true>::type>(a, nw, stream);
+      case 4: return stream_launch<E, D, 4, typename FoldFor<E, D, 4, true>::type>(a, nw, stream);
+      case 8: return stream_launch<E, D, 8, typename FoldFor<E, D, 8, true>::type>(a, nw, stream);
     }
     return hipErrorInvalidValue;
   }

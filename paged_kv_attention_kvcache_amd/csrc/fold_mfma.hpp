@@ -26,6 +26,10 @@
 // col_hi. Keys at or past the context end still zero their V rows for every
 // column; keys inside the context but past a column's end only get
 // probability 0 in that column.
+//
+// L (early exit): each token row is read from the bank of plane
+// min(query plane, the token's exit depth) of the same layer; the fold math
+// is unchanged.
 #pragma once
 #include <climits>
 
@@ -33,12 +37,12 @@
 
 namespace pkv {
 
-template <int G, bool PC = false>
+template <int G, bool PC = false, bool L = false>
 struct MfmaFold {
-  static_assert(PC ? G == 16 : (G == 4 || G == 8),
+  static_assert(PC ? G == 16 && !L : (G == 4 || G == 8),
                 "MFMA fold covers GQA groups of 4 and 8, or 16 prefill columns");
   static constexpr int kPagesPerStep = 2;
-  static constexpr bool kLatest = false;
+  static constexpr bool kLatest = L;
   static constexpr int kDepth = 2;  // steps in flight per wave
   static constexpr int kGroup = G;
   static constexpr int kHeadDim = 128;
@@ -64,6 +68,7 @@ struct MfmaFold {
   // page (-1: none), this lane's K chunks (as in Regs::k) and V chunk.
   int app_page = -1, app_tok = -1;
   uint4 app_k[4], app_v;
+  LatestArgs la{};  // early-exit decode (L only)
 
   __device__ __forceinline__ static bf16x8 as_bf16(const uint4 &x) {
     return __builtin_bit_cast(bf16x8, x);
@@ -147,6 +152,43 @@ struct MfmaFold {
     for (int i = 0; i < 4; ++i) r.v[0][i] = load_kv<C>(v0 + voff + i * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) r.v[1][i] = load_kv<C>(v1 + voff + i * 256);
+  }
+
+  // Byte offset from the query's own bank to the bank that holds token t of
+  // a page whose 16 exit depths are `ex` (byte t = token t): plane
+  // min(la.plane, depth); bytes past the plane (and ones that would be
+  // negative as int8) give the query's own plane, so every address stays in
+  // a bank the call was validated for.
+  __device__ __forceinline__ int64_t exit_delta(const uint4 &ex, int t) const {
+    const uint32_t w = (t >> 2) == 0 ? ex.x : (t >> 2) == 1 ? ex.y : (t >> 2) == 2 ? ex.z : ex.w;
+    const int e = min((int)((w >> (8 * (t & 3))) & 0xffu), la.plane);
+    return e == 0 ? la.d0 : la.d1 + (int64_t)(e - 1) * la.step;
+  }
+
+  // Early-exit variant of load: page0 / page1 with exit depths ex0 / ex1.
+  // This lane's K chunks are all of token l%16; its V rows are tokens
+  // 4(l/16) + i.
+  __device__ __forceinline__ void load_latest(Regs &r, const uint4 *__restrict__ kb,
+                                              const uint4 *__restrict__ vb, int page0,
+                                              const uint4 &ex0, int page1, const uint4 &ex1,
+                                              int hkv, int kvh) const {
+    const size_t t0 = ((size_t)page0 * hkv + kvh) * 256, t1 = ((size_t)page1 * hkv + kvh) * 256;
+    const char *kt[2] = {reinterpret_cast<const char *>(kb + t0),
+                         reinterpret_cast<const char *>(kb + t1)};
+    const char *vt[2] = {reinterpret_cast<const char *>(vb + t0),
+                         reinterpret_cast<const char *>(vb + t1)};
+    const uint4 ex[2] = {ex0, ex1};
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+      const char *k = kt[P] + exit_delta(ex[P], n) + koff;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r.k[P][c] = load_stream(k + c * 64);
+    }
+#pragma unroll
+    for (int P = 0; P < 2; ++P)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.v[P][i] = load_stream(vt[P] + exit_delta(ex[P], 4 * g4 + i) + voff + i * 256);
   }
 
   // Folds pages piA and piB (piB = -1: absent) of the request; keys outside

@@ -117,9 +117,11 @@ struct ValuFold {
   // plane min(la.plane, depth); bytes past the plane (and ones that would be
   // negative as int8) read the query's own plane, so every address stays in
   // a bank the call was validated for.
+  // (One page per step: the second page and its depths are not used.)
   __device__ __forceinline__ void load_latest(Regs &r, const uint4 *__restrict__ kb,
                                               const uint4 *__restrict__ vb, int page,
-                                              const uint4 &ex, int hkv, int kvh) const {
+                                              const uint4 &ex, int, const uint4 &, int hkv,
+                                              int kvh) const {
     const size_t tile = ((size_t)page * hkv + kvh) * TL::kTileVec;
     const char *kt = reinterpret_cast<const char *>(kb + tile);
     const char *vt = reinterpret_cast<const char *>(vb + tile);

@@ -7,9 +7,12 @@
 
 namespace pkv {
 
-template <typename E, int D, int G> struct FoldFor { using type = ValuFold<E, D, G>; };
-template <> struct FoldFor<BF16, 128, 4> { using type = MfmaFold<4>; };
-template <> struct FoldFor<BF16, 128, 8> { using type = MfmaFold<8>; };
+// L: the early-exit variant (each token row read from its own plane's bank).
+template <typename E, int D, int G, bool L = false> struct FoldFor {
+  using type = ValuFold<E, D, G, L>;
+};
+template <bool L> struct FoldFor<BF16, 128, 4, L> { using type = MfmaFold<4, false, L>; };
+template <bool L> struct FoldFor<BF16, 128, 8, L> { using type = MfmaFold<8, false, L>; };
 
 
 }  // namespace pkv

@@ -468,9 +468,6 @@ int paged_decode_latest_attn(const pkv_pool *pool, int32_t plane_id, int32_t lay
   if (exit_stride <= 0 || exit_stride % 16 != 0 || exit_stride < (max_seq_len + 15) / 16 * 16)
     return fail(PKV_EINVAL, "exit_stride %d must be a multiple of 16 covering max_seq_len %d",
                 exit_stride, max_seq_len);
-  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0 ||
-      (num_q_heads / pool->num_kv_heads != 1 && num_q_heads / pool->num_kv_heads != 2))
-    return fail(PKV_EUNSUPPORTED, "early-exit decode supports GQA groups of 1 and 2");
   if (!k_new != !v_new) return fail(PKV_EINVAL, "k_new and v_new must both be given or both NULL");
   if (k_new && ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15))
     return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");

@@ -56,14 +56,16 @@ __device__ __forceinline__ void stream_pages(F &f, typename F::State &st,
     // chunk (odd tail of a 2-page step) reloads the last page and is masked.
     auto page = [&](int k) { return __builtin_amdgcn_readlane(pid, min(k, cnt - 1)); };
     auto index = [&](int k) { return k < cnt ? pi0 + stride * k : -1; };
+    // The 16 exit depths of the k-th page of this chunk (early exit).
+    auto exits = [&](int k) {
+      k = min(k, cnt - 1);
+      return make_uint4(__builtin_amdgcn_readlane(ex.x, k), __builtin_amdgcn_readlane(ex.y, k),
+                        __builtin_amdgcn_readlane(ex.z, k), __builtin_amdgcn_readlane(ex.w, k));
+    };
     auto load = [&](typename F::Regs &r, int s) {
       if constexpr (F::kLatest) {
-        const int k = min(s, cnt - 1);  // one page per step
-        const uint4 e = make_uint4(__builtin_amdgcn_readlane(ex.x, k),
-                                   __builtin_amdgcn_readlane(ex.y, k),
-                                   __builtin_amdgcn_readlane(ex.z, k),
-                                   __builtin_amdgcn_readlane(ex.w, k));
-        f.load_latest(r, kb, vb, page(s), e, hkv, kvh);
+        f.load_latest(r, kb, vb, page(s * S), exits(s * S), page(s * S + S - 1),
+                      exits(s * S + S - 1), hkv, kvh);
       } else {
         f.template load<C>(r, kb, vb, page(s * S), page(s * S + S - 1), hkv, kvh);
       }

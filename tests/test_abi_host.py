@@ -237,7 +237,7 @@ def test_decode_latest_validation(L):
     assert call(ed=FAKE + 8) == pkv.PKV_EINVAL          # not 16-byte aligned
     assert call(stride=40) == pkv.PKV_EINVAL            # not a multiple of 16
     assert call(stride=48) == pkv.PKV_EINVAL            # shorter than max_seq_len
-    assert call(hq=8) == pkv.PKV_EUNSUPPORTED           # group 4
+    assert call(hq=6) == pkv.PKV_EUNSUPPORTED           # group 3
     assert call(layer=0, plane=1) == pkv.PKV_ENOTHELD   # plane 1 does not hold layer 0
     assert call(layer=0, plane=0, max_seq=65) == pkv.PKV_EINVAL  # beyond stride * page_size
 

@@ -2,12 +2,13 @@
 fuzzy minds", section "Can we actually stop early?"): position pos is read
 from plane min(query plane, exit depth of pos) of the same layer.
 
-Covered: every plane of a packed recurrent layer, groups 1 and 2, bf16 and
-fp32, the whole-context, balanced and fixed-partition splits; bitwise
-equalities with the ordinary decode when no token exits before the query's
-plane (including depth bytes past the plane or negative, which read the
-query's plane), and of the fused append with a write followed by the
-early-exit decode."""
+Covered: every plane of a packed recurrent layer, groups 1, 2 (vector
+folds), 4 and 8 (matrix-core fold; fp32 and head_dim 64 take the vector
+fold), bf16 and fp32, the whole-context, balanced, fixed-partition and
+per-partition-block splits; bitwise equalities with the ordinary decode when
+no token exits before the query's plane (including depth bytes past the
+plane or negative, which read the query's plane), and of the fused append
+with a write followed by the early-exit decode."""
 from __future__ import annotations
 
 import numpy as np
@@ -72,6 +73,11 @@ CASES = {
     "g1_balanced": ("bf16", 3, (100, 3000), 4, 4, 128, 0),  # balanced split + combine
     "g2_fixed": ("bf16", 5, (1, 700), 4, 2, 128, 64),       # fixed partitions of 64
     "f32_g2": ("f32", 4, (17, 64), 4, 2, 64, 0),            # tiny fp32 decode shape
+    "g4_whole": ("bf16", 16, (1, 600), 16, 4, 128, 0),      # matrix-core fold, whole
+    "g8_balanced": ("bf16", 3, (100, 3000), 16, 2, 128, 0),  # matrix-core fold, balanced
+    "g8_fixed": ("bf16", 5, (1, 700), 16, 2, 128, 64),      # fixed partitions of 64
+    "g4_block48": ("bf16", 5, (1, 700), 8, 2, 128, 48),     # 3-page partitions: block kernel
+    "f32_g4": ("f32", 4, (17, 300), 8, 2, 64, 0),           # vector fold of group 4
 }
 
 
@@ -90,6 +96,29 @@ def test_latest_matches_oracle(name):
         out, lse = pkv.decode_latest(gp, p, 1, ed, to_dev(q, dtype), table, seq, mx,
                                      partition=partition)
         check(f"latest/{name}/plane{p}", dtype, out, ro, rl, lse)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 4), (16, 2)])
+def test_latest_bitwise_no_exit_groups(hq, hkv):
+    # matrix-core fold: with no token exiting before the query's plane the
+    # early-exit decode is the ordinary decode, bit for bit
+    import torch
+
+    case, op, gp, stride = setup(5, "bf16", 8, (1, 700), hq, hkv, 128)
+    table, seq = i32_dev(case.page_table), i32_dev(case.seq_lens)
+    mx = int(case.seq_lens.max())
+    rng = np.random.default_rng(6)
+    for p in (0, PLANES - 1):
+        q = to_dev(case.banks[(p, 1)].q, "bf16")
+        deep = rng.integers(p, 128, size=(case.batch, stride)).astype(np.int8)
+        deep[:, ::5] = -3
+        for partition in (0, 64):
+            say(f"latest no-exit hq={hq} hkv={hkv} plane={p} partition={partition}")
+            a, la = pkv.decode_latest(gp, p, 1, depth_dev(deep), q, table, seq, mx,
+                                      partition=partition)
+            b, lb = pkv.decode(gp, p, 1, q, table, seq, mx, partition=partition)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(a), bits(b)) and np.array_equal(bits(la), bits(lb))
 
 
 def test_latest_bitwise_equalities():
