@@ -1,17 +1,24 @@
 #!/bin/bash
 # Collects, on an MI355X, the rocprofv3 runs behind profiles/ and writes their
 # summaries there. Run from the repository root with the library built:
-#   bash paged_kv_attention_kvcache_amd/collect_profiles.sh OUT
+#   bash paged_kv_attention_kvcache_amd/collect_profiles.sh OUT [STEP ...]
 # OUT receives the raw rocprofv3 output (large; not committed). Every run is
-# one of the commands named in the summaries' headers.
+# one of the commands named in the summaries' headers. With STEP names only
+# those runs are made (the raw output of several invocations can be gathered
+# into one OUT); the last step, "summaries", needs every run in OUT and
+# needs no GPU.
 set -o pipefail
-OUT=${1:?usage: collect_profiles.sh OUT}
+OUT=${1:?usage: collect_profiles.sh OUT [STEP ...]}
+shift
+ONLY=" $* "
 R=$(pwd)
 mkdir -p "$OUT"
 export TMPDIR=${TMPDIR:-/tmp}
+want() { [ "$ONLY" = "  " ] || [[ "$ONLY" == *" $1 "* ]]; }
 step() {
   local name=$1
   shift
+  want "$name" || return 0
   echo "== $name $(date +%T)"
   "$@" > "$OUT/$name.log" 2>&1 || { echo "$name failed"; tail -20 "$OUT/$name.log"; exit 1; }
 }
@@ -42,5 +49,6 @@ pmc decode_tcc "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_s
   python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-baseline --no-prefill
 pmc decode_sq "SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INST_LEVEL_VMEM SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_BUSY_CYCLES SQ_WAVES" \
   python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-baseline --no-prefill
+want summaries || exit 0
 echo "== summaries $(date +%T)"
 python3 -m paged_kv_attention_kvcache_amd.rocprof_summary write "$OUT" --profiles "$R/profiles"

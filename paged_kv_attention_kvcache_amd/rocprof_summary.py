@@ -45,9 +45,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 WORKLOAD_KERNELS = {
     "ouro": [("decode_whole<pkv::BF16, pkv::ValuFold<pkv::BF16, 128, 2, false>", None)],
     "huginn": [("decode_whole<pkv::BF16, pkv::ValuFold<pkv::BF16, 128, 1, false>", None)],
-    "longctx": [("decode_stream<pkv::BF16, pkv::MfmaFold<8, false>", None),
+    "longctx": [("decode_stream<pkv::BF16, pkv::MfmaFold<8, false, false>", None),
                 ("decode_stream_combine<pkv::BF16, 8>", None)],
-    "longctx_p512": [("decode_parts<pkv::BF16, pkv::MfmaFold<8, false>", None),
+    "longctx_p512": [("decode_parts<pkv::BF16, pkv::MfmaFold<8, false, false>", None),
                      ("decode_parts_combine<pkv::BF16, 8>", None)],
     "prefill_cold2048": [("prefill_mfma", 131072)],
     "prefill_8x2048": [("prefill_mfma", 524288)],

@@ -116,7 +116,7 @@ def test_workload_figures(tmp_path):
     # + combine 13 us) and the 8 x 2048 prefill (grid 524288; the 131072-grid
     # prefill calls belong to another workload). Copy probe: scales 2 and 1.
     base = str(tmp_path)
-    stream = "void pkv::decode_stream<pkv::BF16, pkv::MfmaFold<8, false> >(uint4 const*)"
+    stream = "void pkv::decode_stream<pkv::BF16, pkv::MfmaFold<8, false, false> >(uint4 const*)"
     comb = "void pkv::decode_stream_combine<pkv::BF16, 8>(int)"
     pre = "void pkv::prefill_mfma<4, 2, 2048>(uint4 const*)"
     st = os.path.join(base, "st")
@@ -200,3 +200,23 @@ def test_write_profiles_from_a_collection(tmp_path):
     assert "l1_to_l2_latency_clk     500" in text and "l2_to_mem_latency_clk    1400" in text
     for n in names:
         assert "collect_profiles.sh" in (prof / n).read_text()
+
+
+def test_workload_kernels_name_kernels_of_the_library():
+    # every kernel name the per-workload figures look for is the demangled
+    # name of a kernel the built library holds (a renamed template would
+    # otherwise drop its workload from the summaries without an error)
+    import subprocess
+
+    import paged_kv_attention_kvcache_amd as pkv
+
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.skip("library not built")
+    out = subprocess.run(["nm", "-C", "--defined-only", pkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    kernels = [ln.split(" ", 2)[2] for ln in out.splitlines()
+               if " V void pkv::" in ln and "__device_stub__" not in ln]
+    assert kernels
+    for wl, ks in rs.WORKLOAD_KERNELS.items():
+        for substr, _ in ks:
+            assert any(substr in k for k in kernels), (wl, substr)
