@@ -356,9 +356,13 @@ class PrefillWorkload:
 
     def run(self, chunks, bank, write=True):
         """write=True: paged_kv_write then paged_prefill_attn per chunk; False:
-        the attention alone; "extend": paged_extend_attn (one call)."""
+        the attention alone; "extend": paged_extend_attn (one call);
+        "store_only": the paged_kv_write calls alone."""
         pkv = self.pkv
         for c in chunks:
+            if write == "store_only":
+                pkv.kv_write(self.pool, bank, 0, c["k"], c["v"], c["slots"])
+                continue
             if write == "extend":
                 pkv.extend(self.pool, bank, 0, c["k"], c["v"], c["slots"], c["q"], c["cu"],
                            self.table_d, c["seq"], c["q_len"], c["hi"], out=c["o"],
@@ -381,8 +385,9 @@ SUPPLEMENTARY = ("cold_2048x8_chunk2048", 8, 2048, 2048, 0)
 
 def time_prefill_case(wl, chunks, reps):
     """Per call of the case (all its chunks): write-then-attend, the one-call
-    extend, and the attention alone, each over reps rounds of the bank
-    rotation, between HIP events on the stream the library launches on."""
+    extend, the attention alone and the store_kv alone, each over reps rounds
+    of the bank rotation, between HIP events on the stream the library
+    launches on."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -390,7 +395,7 @@ def time_prefill_case(wl, chunks, reps):
         wl.run(chunks, b)
     torch.cuda.synchronize()
     out = {}
-    for write in (True, "extend", False):
+    for write in (True, "extend", False, "store_only"):
         a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nbk = wl.nb
         a.record(stream)
@@ -399,7 +404,7 @@ def time_prefill_case(wl, chunks, reps):
         e.record(stream)
         torch.cuda.synchronize()
         key = {True: "write_then_attend", "extend": "extend_one_call",
-               False: "attend_only"}[write]
+               False: "attend_only", "store_only": "store_kv_only"}[write]
         out[key] = a.elapsed_time(e) / 1e3 / (reps * nbk)
     return out
 
@@ -430,6 +435,7 @@ def cpu_prefill(wl, chunks, budget_s):
         calls += 1
     return {"value": round(done / spent / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(os.environ.get("OMP_NUM_THREADS", "1")), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{calls} x the first call of the case ({wl.prompts} prompts x "
                       f"{c['q_len']} query rows, {wl.heads} heads, fp64 oracle), {spent:.2f} s"}
 
@@ -451,7 +457,14 @@ def run_prefill(reps=3, supplementary=True, cpu_budget=0.0):
         hbm = sum(c["hi"] * wl.prompts * 2 * wl.heads * wl.D * 2 + 2 * c["q"].numel() * 2
                   for c in chunks)
         t = time_prefill_case(wl, chunks, reps)
-        out = {}
+        # store_kv: the chunk's K and V read from the caller's buffers and
+        # written to their slots
+        kv = sum(c["k"].numel() + c["v"].numel() for c in chunks) * 2 * 2
+        st = t.pop("store_kv_only")
+        out = {"store_kv": {"us": round(st * 1e6, 2), "bytes": kv,
+                            "GBps": round(kv / st / 1e9, 1),
+                            "hbm_frac": round(kv / st / 1e9 / HBM_PEAK_GBS, 4),
+                            "kernel": "kv_write_kernel (paged_kv_write per chunk)"}}
         for key, sec in t.items():
             out[key] = {"us": round(sec * 1e6, 2), "TFLOPs": round(flops / sec / 1e12, 2),
                         "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -618,6 +631,7 @@ def run_tiny(reps=500, cpu_budget=0.0):
         res["cpu_baseline"] = {
             "value": round(spent / calls * 1e6, 3), "unit": "us per call",
             "cores": int(os.environ.get("OMP_NUM_THREADS", "1")), "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": f"{calls} calls of the whole tiny decode (4 requests, 4 heads; the "
                       f"oracle's attention alone, its store_kv done once), {spent:.2f} s"}
     return res
@@ -658,6 +672,17 @@ def run_page_mgr(reps=200):
 
 # --------------------------------------------------------------------------- CPU baseline
 
+def cpu_model() -> str:
+    """The host CPU's model name (as /proc/cpuinfo states it)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_threads() -> int:
     """Threads the oracle runs with: every core this process may use."""
     threads = len(os.sched_getaffinity(0))
@@ -691,7 +716,7 @@ def cpu_baseline(wl: DecodeWorkload, budget_s: float = 8.0):
             f"{wl.batch} requests, all heads" if rows == wl.batch else
             f"the first {rows} of the {wl.batch} requests of one call, all heads")
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{calls} oracle decode calls over {what}; logical KV bytes of those "
                       f"calls / {spent:.1f} s (fp64)"}
 
