@@ -40,6 +40,9 @@ pmc all_write WRITE_SIZE python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-bas
 # Matrix-core and instruction counters of the prefill kernels, L2 hit rates.
 pmc prefill_engine "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES" \
   python3 "$R/bench.py" --prefill-only --no-cpu-baseline
+# What the prefill step waits on: engine clock, matrix-core and LDS activity, waits.
+pmc prefill_pipeline "SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_WAIT_ANY SQ_WAVE_CYCLES" \
+  python3 "$R/bench.py" --prefill-only --no-cpu-baseline
 pmc all_l2 "TCC_HIT_sum TCC_MISS_sum" python3 "$R/bench.py" --steps 1 --warmup 1 --no-cpu-baseline
 # What bounds the decode kernels: L1->L2 and L2->memory read latency, TLB
 # misses, instruction counts and waits (decode workloads only).

@@ -208,13 +208,20 @@ def workloads(stats_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir,
     return out
 
 
-def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.4e9) -> list[dict]:
+def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.4e9,
+                    cus: int = 256) -> list[dict]:
     """Per launch shape of the kernels matching `kernel`: the mean of each
     counter per dispatch and what follows from them. SQ_VALU_MFMA_BUSY_CYCLES
     sums matrix-core busy clocks over every SIMD, so mfma_busy = that / (SIMDs
     x dispatch time x the nominal 2.4 GHz engine clock), the fraction of the
     dense MFMA peak the busy time could deliver; l2_hit = TCC_HIT / (TCC_HIT +
-    TCC_MISS), summed over the dies' L2 caches."""
+    TCC_MISS), summed over the dies' L2 caches. With SQ_BUSY_CU_CYCLES (the
+    busy cycles of the CUs, summed): clock_ghz = those of one CU / time (the
+    engine clock, while every CU is busy for the whole dispatch);
+    mfma_busy_at_clock = the matrix-core busy fraction at that clock;
+    lds_read_B_per_clk_cu = SQ_INSTS_LDS_LOAD_BANDWIDTH (64-byte units) per
+    CU-cycle; lds_active = SQ_LDS_IDX_ACTIVE per CU-cycle; wave_wait_frac =
+    SQ_WAIT_ANY / SQ_WAVE_CYCLES."""
     rows = csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv"))))
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     dur = collections.defaultdict(dict)
@@ -235,11 +242,26 @@ def engine_counters(d: str, kernel: str, simds: int = 1024, clock_hz: float = 2.
             res["l2_hit"] = m["TCC_HIT_sum"] / (m["TCC_HIT_sum"] + m["TCC_MISS_sum"])
         if "SQ_INSTS_VALU" in m and m.get("SQ_INSTS_MFMA"):
             res["valu_per_mfma"] = m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"]
+        busy = m.get("SQ_BUSY_CU_CYCLES", 0.0)
+        if busy > 0:
+            cu_cycles = busy / cus  # one CU's busy cycles
+            res["clock_ghz"] = cu_cycles / t / 1e9
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                res["mfma_busy_at_clock"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cu_cycles
+            if "SQ_INSTS_LDS_LOAD_BANDWIDTH" in m:
+                res["lds_read_B_per_clk_cu"] = m["SQ_INSTS_LDS_LOAD_BANDWIDTH"] * 64 / busy
+            if "SQ_LDS_IDX_ACTIVE" in m:
+                res["lds_active"] = m["SQ_LDS_IDX_ACTIVE"] / busy
+        if m.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in m:
+            res["wave_wait_frac"] = m["SQ_WAIT_ANY"] / m["SQ_WAVE_CYCLES"]
         out.append(res)
     return out
 
 
 COLLECT = "bash paged_kv_attention_kvcache_amd/collect_profiles.sh OUT"
+PIPELINE_COUNTERS = ("SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+                     "SQ_ACTIVE_INST_VALU SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS_LOAD_BANDWIDTH "
+                     "SQ_WAIT_ANY SQ_WAVE_CYCLES")
 
 
 def _stats_text(d: str) -> str:
@@ -322,6 +344,19 @@ def write_profiles(out: str, profiles: str) -> None:
         for k, v in r.items():
             if k not in ("kernel", "grid", "dispatches"):
                 body.append(f"    {k:28s} {v:.6g}")
+    body.append(f"""
+# Second pass, what the step's pipeline waits on:
+#   rocprofv3 --pmc {PIPELINE_COUNTERS} --output-format csv -d OUT/prefill_pipeline -o run -- python3 bench.py --prefill-only --no-cpu-baseline
+# clock_ghz = SQ_BUSY_CU_CYCLES / 256 CUs / time; mfma_busy_at_clock = SQ_VALU_MFMA_BUSY_CYCLES /
+# 1024 SIMDs / the CU cycles; lds_read_B_per_clk_cu = SQ_INSTS_LDS_LOAD_BANDWIDTH x 64 B per
+# CU-cycle (it matches the kernel's 32 KiB of LDS reads per wave-step to within 2%);
+# lds_active = SQ_LDS_IDX_ACTIVE per CU-cycle; wave_wait_frac = SQ_WAIT_ANY / SQ_WAVE_CYCLES.""")
+    if os.path.isdir(j("prefill_pipeline")):
+        for r in engine_counters(j("prefill_pipeline"), "prefill"):
+            body.append(f"{r['kernel']}  grid {r['grid']}  ({r['dispatches']} dispatches)")
+            for k, v in r.items():
+                if k not in ("kernel", "grid", "dispatches"):
+                    body.append(f"    {k:28s} {v:.6g}")
     with open(os.path.join(profiles, "prefill_engine_counters.txt"), "w") as fh:
         fh.write(hdr + "\n".join(body) + "\n")
     hdr = f"""# L2 hit rates per kernel and launch shape, library sources {h}: TCC_HIT / (TCC_HIT +

@@ -177,6 +177,12 @@ def test_write_profiles_from_a_collection(tmp_path):
                                       [2, 524288, pre, "WRITE_SIZE", 100.0, 0, 10]])
     _counters(str(out / "prefill_engine"), [[1, 524288, pre, "SQ_VALU_MFMA_BUSY_CYCLES", 1e6,
                                              0, 100000]])
+    _counters(str(out / "prefill_pipeline"),
+              [[1, 524288, pre, "SQ_BUSY_CU_CYCLES", 256 * 2e5, 0, 100000],
+               [1, 524288, pre, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 8e4, 0, 100000],
+               [1, 524288, pre, "SQ_INSTS_LDS_LOAD_BANDWIDTH", 256 * 2e5 / 64 * 50, 0, 100000],
+               [1, 524288, pre, "SQ_WAIT_ANY", 30.0, 0, 100000],
+               [1, 524288, pre, "SQ_WAVE_CYCLES", 100.0, 0, 100000]])
     _counters(str(out / "all_l2"), [[1, 131072, ouro, "TCC_HIT_sum", 10.0, 0, 10],
                                    [1, 131072, ouro, "TCC_MISS_sum", 90.0, 0, 10]])
     _counters(str(out / "decode_tcp"), [[1, 131072, ouro, "TCP_TCC_READ_REQ_LATENCY_sum", 5000.0,
@@ -196,6 +202,12 @@ def test_write_profiles_from_a_collection(tmp_path):
     # the copy probe of 1 GiB read 512 KiB of FETCH_SIZE and 1024 KiB of WRITE_SIZE
     assert k["workloads"]["prefill_8x2048"]["hbm_bytes_per_call"] == \
         300 * 1024 * 2048 + 100 * 1024 * 1024
+    # 2e5 busy cycles per CU over a 100 us dispatch: 2 GHz; the matrix cores
+    # 8e4 of them (40%); 50 B of LDS reads per CU-cycle; waves wait 30%
+    pipe = (prof / "prefill_engine_counters.txt").read_text()
+    for want in ("clock_ghz                    2", "mfma_busy_at_clock           0.4",
+                 "lds_read_B_per_clk_cu        50", "wave_wait_frac               0.3"):
+        assert want in pipe, want
     text = (prof / "decode_memory_counters.txt").read_text()
     assert "l1_to_l2_latency_clk     500" in text and "l2_to_mem_latency_clk    1400" in text
     for n in names:
