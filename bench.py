@@ -476,14 +476,14 @@ def run_prefill(reps=3, supplementary=True, cpu_budget=0.0):
         sec = t["attend_only"] / len(chunks)
         if name == "cold_chunk2048":
             out["roofline"] = roofline(
-                "prefill_cold2048", "prefill_mfma<4, 2, 2048> (8 x 512 rows, 4 tiles each)",
+                "prefill_cold2048", "prefill_mfma<4, 2, 2048, 2> (8 x 512 rows, 4 tiles each)",
                 flops / sec / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma", flops, sec,
                 hbm_frac=round(hbm / sec / 1e9 / HBM_PEAK_GBS, 4),
                 note="at the ridge: 128 flop per algorithmic byte; the HBM floor of the "
                      "call is 16.8 us")
         if name == SUPPLEMENTARY[0]:
             out["roofline"] = roofline(
-                "prefill_8x2048", "prefill_mfma<4, 2, 2048> (8 x 2048 rows, 16 tiles each)",
+                "prefill_8x2048", "prefill_mfma<4, 2, 2048, 2> (8 x 2048 rows, 16 tiles each)",
                 flops / sec / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma", flops, sec)
         if cpu_budget > 0 and name in ("cold_chunk2048", "suffix16_over_496"):
             log(f"cpu baseline (oracle): prefill {name} ...")

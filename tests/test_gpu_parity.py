@@ -333,6 +333,26 @@ def test_prefill_short_chunks(hq, hkv):
     _prefill_compare(f"short/{hq}x{hkv}", case, chunks, gp, op)
 
 
+@pytest.mark.parametrize("hq,hkv,chunk", [(32, 32, 64), (16, 4, 64), (16, 2, 64), (16, 2, 65)])
+def test_prefill_64_row_tiles(hq, hkv, chunk):
+    # calls with at most 64 rows per request run on 64-row tiles (one block of
+    # 16 query rows per wave), 65 on 128-row tiles: ragged q_lens of 1 to 130
+    # over cached prefixes, a request with no rows, a page-tail prompt, and
+    # several chunks in a row
+    say(f"prefill 64-row tiles {hq}/{hkv} chunk {chunk}")
+    prompts = [600, 64, 1, 300, 130, 1000, 17, 47]
+    q_lens = [130, 64, 1, 63, 0, 33, 17, 47]
+    starts = [n - min(ql, n) for n, ql in zip(prompts, q_lens)]
+    case = synth.make_prefill_case(17, "bf16", prompts, hq, hkv, 128, q_scale=2.0)
+    gp, op = gpu_pool(case.layout), oracle_pool(case.layout)
+    k, v, sl = synth.prefix_writes(case, starts)
+    write(gp, 0, 0, k, v, sl, "bf16")
+    oracle.kv_write(op, 0, 0, k, v, sl)
+    chunks = synth.chunk_schedule(case, chunk, start=starts)
+    assert int(np.diff(chunks[0].cu_q_lens).max()) == chunk
+    _prefill_compare(f"tiles64/{hq}x{hkv}/{chunk}", case, chunks, gp, op)
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,D", [("f32", 8, 2, 64), ("bf16", 8, 1, 128),
                                             ("f32", 2, 2, 128), ("bf16", 4, 2, 64)])
 def test_prefill_ragged(dtype, hq, hkv, D):
